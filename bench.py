@@ -1,0 +1,224 @@
+"""Benchmark: one decode step of paged attention on one MI355X.
+
+A step is the whole hot path over one batch: clone shared blocks (copy_blocks, when the
+workload has copy-on-write pairs), write each sequence's newest K/V (reshape_and_cache),
+then paged decode attention (pa_decode: partition kernel + split-sequence reduce). Inputs
+are seeded synthetic data resident in HBM before timing starts; successive steps rotate
+over R replicas of (pool, q, tables, ...) so the working set exceeds the 256 MB Infinity
+Cache. Prints ONE JSON line.
+
+  value        effective KV GB/s of the step: sum_b L_b * Hkv * D * 2 * elt / step time
+  roofline     pa_decode alone: the same KV bytes / its mean duration (HIP events around
+               each call, on the stream it runs on) against 8 TB/s
+  cpu_baseline the fp64 oracle (OpenMP, all host threads) on the same step, repeated for a
+               bounded ~10 s sample
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attention effective KV GB/s (% of HBM peak); µs per decode step"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pa_decode.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_298_amd", "csrc", "pa_decode.hip")
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _to_dev(a, torch, dev):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+def _decode_source_sha():
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic_for(config_name):
+    """HBM bytes per pa_decode launch from the committed rocprofv3 counter summary, only
+    while the kernel source is the one the counters were taken from."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != _decode_source_sha():
+        return None
+    entry = rec.get("workloads", {}).get(config_name)
+    return entry.get("bytes_per_launch") if entry else None
+
+
+def _cpu_baseline(wl, budget_s):
+    from oracle import oracle as orc
+    threads = orc.max_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        kc, vc = wl.k_cache, wl.v_cache
+        if wl.cow_pairs.shape[0]:
+            kc, vc = orc.copy_blocks(kc, vc, wl.cow_pairs)
+        kc, vc = orc.reshape_and_cache(kc, vc, wl.new_key, wl.new_value, wl.slot_mapping)
+        orc.decode(wl.q, kc, vc, wl.block_tables, wl.seq_lens, wl.scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 200:
+            break
+    per = el / reps
+    return {"value": round(wl.kv_bytes() / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds_per_step": round(per, 4),
+            "sample": f"the full step (cache write + fp64 decode of all {wl.B} sequences) "
+                      f"repeated {reps}x, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload 1-5 (2 = the headline)")
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode path "
+              "shards by sequence or KV head with no exchange; only N=1 is built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_cache_298_amd import pa
+    from paged_kv_cache_298_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    _log(f"generating workload {args.config}")
+    wl = W.config(args.config, poison=False)
+    kv_bytes = wl.kv_bytes()
+    per_replica = 2 * wl.k_cache.nbytes + wl.q.nbytes + wl.block_tables.nbytes
+    R = args.replicas or max(2, math.ceil((1 << 30) / per_replica))
+    _log(f"{wl.name}: B={wl.B} kv_bytes={kv_bytes} pool={wl.num_blocks} blocks, replicas={R}")
+
+    reps = []
+    ws_bytes = pa.pa_decode_workspace_bytes(wl.B, wl.Hq, wl.D, wl.block_size, wl.max_blocks)
+    for _ in range(R):
+        reps.append(dict(
+            q=_to_dev(wl.q, torch, dev), k=_to_dev(wl.k_cache, torch, dev),
+            v=_to_dev(wl.v_cache, torch, dev), bt=_to_dev(wl.block_tables, torch, dev),
+            sl=_to_dev(wl.seq_lens, torch, dev), nk=_to_dev(wl.new_key, torch, dev),
+            nv=_to_dev(wl.new_value, torch, dev), slots=_to_dev(wl.slot_mapping, torch, dev),
+            pairs=_to_dev(wl.cow_pairs, torch, dev) if wl.cow_pairs.shape[0] else None,
+            out=torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev),
+            ws=torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(r):
+        if r["pairs"] is not None:
+            pa.pa_copy_blocks(r["k"], r["v"], r["pairs"], stream=stream)
+        pa.pa_reshape_and_cache(r["k"], r["v"], r["nk"], r["nv"], r["slots"], stream=stream)
+        pa.pa_decode(r["out"], r["q"], r["k"], r["v"], r["bt"], r["sl"], wl.scale,
+                     workspace=r["ws"], stream=stream)
+
+    def decode_only(r):
+        pa.pa_decode(r["out"], r["q"], r["k"], r["v"], r["bt"], r["sl"], wl.scale,
+                     workspace=r["ws"], stream=stream)
+
+    # ---- whole step
+    for i in range(args.warmup):
+        step(reps[i % R])
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(reps[i % R])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    _log(f"step: {ms_step * 1e3:.1f} us (events), {wall_ms * 1e3:.1f} us (wall)")
+
+    # ---- pa_decode alone: events around every call, on its stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for i in range(args.warmup):
+        decode_only(reps[i % R])
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        decode_only(reps[i % R])
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    dec_us = np.array([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)])
+    dec_mean = float(dec_us.mean())
+    _log(f"pa_decode: mean {dec_mean:.1f} us, p10 {np.percentile(dec_us, 10):.1f}, "
+         f"p50 {np.median(dec_us):.1f}, p90 {np.percentile(dec_us, 90):.1f}")
+
+    # ---- hot (one replica, Infinity Cache may help) for context
+    hot = []
+    for i in range(args.warmup):
+        decode_only(reps[0])
+    torch.cuda.synchronize()
+    for i in range(min(args.steps, 50)):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        decode_only(reps[0])
+        e.record(stream)
+        hot.append((s, e))
+    torch.cuda.synchronize()
+    hot_us = float(np.mean([s.elapsed_time(e) * 1e3 for s, e in hot]))
+
+    achieved = kv_bytes / (dec_mean * 1e-6) / 1e9
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log("cpu baseline (oracle)")
+        cpu = _cpu_baseline(wl, args.cpu_seconds)
+
+    traffic = _traffic_for(wl.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": W.CONFIG_NAMES[args.config], "global_batch": wl.B,
+                   "kv_bytes_per_step": kv_bytes, "replicas_rotated": R,
+                   "step": "copy_blocks (if CoW pairs) + reshape_and_cache + pa_decode"},
+        "roofline": {"bound": "hbm", "kernel": "pa_decode (partition + reduce launches)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "decode_us_mean": round(dec_mean, 2),
+                     "decode_us_p10": round(float(np.percentile(dec_us, 10)), 2),
+                     "decode_us_p90": round(float(np.percentile(dec_us, 90)), 2),
+                     "decode_us_hot_one_replica": round(hot_us, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

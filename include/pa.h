@@ -1,0 +1,195 @@
+/*
+ * pa.h -- C ABI of libpa: paged KV-cache decode attention for AMD MI355X (gfx950).
+ *
+ * Sources (the web pages the method is taken from; cited below by tag and section):
+ *   [P1] "PagedAttention", inferensys.com glossary entry
+ *   [P2] "Paged Attention" tutorial, infra.pidoku.co.in (inference engineering, vLLM, file 10)
+ *   [P4] "PagedAttention & KV-Cache Management in High-Throughput LLM Serving",
+ *        subroutine-cs.cc
+ *
+ * Conventions for every entry point
+ *   - Device pointers are owned by the caller (allocated through any HIP allocator; the
+ *     library never allocates device memory). Host pointers are read during the call only.
+ *   - Tensors are dense, row-major, with the shapes given. Cache base pointers and q must
+ *     be 16-byte aligned; block_tables, seq_lens and slot_mapping 4-byte aligned.
+ *   - Cache layout, K and V alike: [num_blocks, num_kv_heads, block_size, head_dim]. Each
+ *     (physical block, KV head) is one contiguous [block_size, head_dim] tile.
+ *   - Element types (kv_dtype): PA_F32 (IEEE binary32) or PA_BF16 (bfloat16, 16 raw bits).
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream). Kernel entry points
+ *     are asynchronous: they validate, enqueue and return.
+ *   - Return value: PA_OK or a negative PA_ERR_* code. Argument checks are pure host code
+ *     and run before any HIP call; on an error nothing is enqueued and pa_last_error()
+ *     describes it (thread-local). Device-resident data (table entries, lengths, slots)
+ *     is not read on the host: entries outside their documented range give unspecified
+ *     results for the rows they touch but never an access outside the buffers.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+/* element types */
+#define PA_F32 0
+#define PA_BF16 1
+
+/* status codes */
+#define PA_OK 0
+#define PA_ERR_INVALID_ARG (-1) /* null pointer, bad shape, misalignment, small workspace */
+#define PA_ERR_UNSUPPORTED (-2) /* valid but not built: head_dim, block_size, group size */
+#define PA_ERR_NO_BLOCKS (-3)   /* allocator: not enough free blocks */
+#define PA_ERR_HIP (-4)         /* the HIP runtime reported an error at launch */
+
+/* ------------------------------------------------------------------ decode attention */
+
+/*
+ * pa_decode -- paged decode attention over a ragged batch ([P1] "Interpret Block Tables"
+ * and "Handle Variable-Length Sequences"; [P2] section 5 "The kernel side"; [P4] section 1,
+ * the decode phase).
+ *
+ * For sequence b and query head h, with G = Hq / Hkv and KV head g = h / G (consecutive
+ * query heads share a KV head) and L = seq_lens[b]:
+ *   token t < L is read from physical block block_tables[b][t / block_size], slot
+ *   t % block_size;  s_t = scale * <q[b,h,:], K_t>;  out[b,h,:] = sum_t softmax(s)_t V_t.
+ * L == 0 gives out[b,h,:] = 0. Slots past L in the last block and table entries past
+ * ceil(L / block_size) are never read.
+ *
+ *   out           device float [B, Hq, D] (always fp32)
+ *   q             device [B, Hq, D], element type kv_dtype
+ *   k_cache       device [num_blocks, Hkv, block_size, D]
+ *   v_cache       device, same shape and type as k_cache
+ *   block_tables  device int32 [B, max_blocks]; entries j < ceil(L_b / block_size) must
+ *                 lie in [0, num_blocks)
+ *   seq_lens      device int32 [B]; 0 <= L_b <= max_blocks * block_size
+ *   scale         softmax scale, applied in fp32 to the fp32 dot product
+ *   workspace     device scratch of at least pa_decode_workspace_bytes(...) bytes, 256-byte
+ *                 aligned (may be NULL when that size is 0); it holds split-sequence
+ *                 partial results and needs no initialisation
+ * Supported: D in {64, 128}; block_size in {16, 32, 64}; G in {1, 2, 4, 8, 16}; others
+ * return PA_ERR_UNSUPPORTED. The result is deterministic: repeated calls give identical
+ * bits, whatever the physical placement of the blocks.
+ */
+int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                  int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                  int32_t max_blocks, float scale, int32_t kv_dtype, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes pa_decode needs for these sizes (0 when no sequence can span more than
+ * one partition). An upper bound taken from the host-known max_blocks.
+ */
+size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t block_size,
+                                 int32_t max_blocks);
+
+/*
+ * Tokens per partition that pa_decode uses for these sizes (a sequence longer than this
+ * is split into partitions whose partial softmax results are combined exactly).
+ */
+int32_t pa_decode_partition_tokens(int32_t block_size, int32_t max_blocks);
+
+/*
+ * Process-wide override of the partition length, for tuning sweeps and tests: tokens must
+ * be 0 (automatic) or a multiple of 64 in [64, 8192]. Not thread-safe; affects calls made
+ * after it returns, including pa_decode_workspace_bytes.
+ */
+int32_t pa_set_partition_tokens(int32_t tokens);
+
+/* ------------------------------------------------------------------ cache write */
+
+/*
+ * pa_reshape_and_cache -- write new tokens' K and V into their physical slots. Slot s is
+ * the flat index table[pos / block_size] * block_size + pos % block_size of [P2] section 4
+ * (PhysicalIndex); the row goes to block s / block_size, offset s % block_size. A bit copy.
+ *
+ *   k_cache, v_cache  device [num_blocks, Hkv, block_size, D], written
+ *   key, value        device [T, Hkv, D]
+ *   slot_mapping      device int32 [T]; s < 0 skips the token (padding); non-negative slots
+ *                     must be distinct; slots >= num_blocks * block_size are skipped
+ * T == 0 is a no-op. Supported: D a multiple of 8 (bf16) or 4 (fp32), up to 512.
+ */
+int32_t pa_reshape_and_cache(void* k_cache, void* v_cache, const void* key, const void* value,
+                             const int32_t* slot_mapping, int32_t T, int32_t Hkv, int32_t D,
+                             int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                             void* stream);
+
+/* ------------------------------------------------------------------ copy-on-write clone */
+
+/*
+ * pa_copy_blocks -- copy whole physical blocks, K and V, all heads and slots: the clone
+ * taken before writing into a shared block ([P2] section 5 "Copy-on-write sharing"; [P4]
+ * section 3). A bit copy.
+ *
+ *   block_pairs  device int32 [N, 2] of (src, dst); destinations must be distinct and no
+ *                destination may also be a source, so the order of the copies is
+ *                irrelevant; a pair with an index outside [0, num_blocks) is skipped
+ * N == 0 is a no-op.
+ */
+int32_t pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t N,
+                       int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                       int32_t kv_dtype, void* stream);
+
+/* ------------------------------------------------------------------ status */
+
+const char* pa_status_string(int32_t status);
+/* message of the last failed call on this thread ("" if none) */
+const char* pa_last_error(void);
+int32_t pa_abi_version(void);
+
+/* ------------------------------------------------------------------ host block allocator */
+
+/*
+ * A refcounted allocator of physical block ids that builds block tables on the host
+ * ([P2] section 4 "Tiny example": free stack, Allocate, Free, Fork, AppendToken,
+ * PhysicalIndex; [P2] section 5 "Copy-on-write sharing"; [P4] sections 3-4). Host memory
+ * only; an allocator object is not thread-safe. Every failing call leaves it unchanged.
+ *
+ * The free list is a stack; initial_free_order (nullable, num_blocks distinct ids) lists
+ * it bottom to top, default num_blocks-1 ... 0, so the first allocation of n blocks
+ * returns ids n-1 ... 0 in that order.
+ */
+typedef struct pa_allocator pa_allocator;
+
+pa_allocator* pa_alloc_create(int32_t num_blocks, int32_t block_size,
+                              const int32_t* initial_free_order);
+void pa_alloc_destroy(pa_allocator* a);
+/* all-or-nothing: n blocks from the top of the stack, refcount 1 each, into out[n];
+ * PA_ERR_NO_BLOCKS ("out of KV blocks: need n, have m") if fewer are free */
+int32_t pa_alloc_allocate(pa_allocator* a, int32_t n, int32_t* out);
+/* refcount - 1 for each listed block; a block whose count reaches 0 is pushed on the
+ * stack; a block freed more often than it is referenced -> PA_ERR_INVALID_ARG */
+int32_t pa_alloc_free(pa_allocator* a, const int32_t* blocks, int32_t n);
+/* refcount + 1 for each listed (allocated) block; out[n] receives the same ids (the new
+ * sequence's table); out may equal blocks */
+int32_t pa_alloc_fork(pa_allocator* a, const int32_t* blocks, int32_t n, int32_t* out);
+/*
+ * Append one token to a sequence whose table is table[0 .. *n_table) (capacity table_cap)
+ * and whose length is *seq_len. With pos = *seq_len and j = pos / block_size:
+ *   j == *n_table: a fresh block is allocated and appended;
+ *   j <  *n_table and table[j] is shared (refcount > 1): a fresh block replaces it, the
+ *                 old block's count drops by one, and when pos % block_size != 0 the pair
+ *                 (old, fresh) is returned as the copy to make before writing;
+ *   otherwise the token goes into table[j] in place.
+ * *out_slot = table[j] * block_size + pos % block_size; *seq_len += 1. *out_cow_src and
+ * *out_cow_dst are -1 when no copy is needed.
+ */
+int32_t pa_alloc_append_token(pa_allocator* a, int32_t* table, int32_t* n_table,
+                              int32_t table_cap, int32_t* seq_len, int32_t* out_slot,
+                              int32_t* out_cow_src, int32_t* out_cow_dst);
+/* current refcount of a block (0 if free), or PA_ERR_INVALID_ARG for an id out of range */
+int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block);
+int32_t pa_alloc_num_free(const pa_allocator* a);
+/* copies the free stack, bottom to top, into out (capacity cap); returns its length */
+int32_t pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,243 @@
+// pa_api.cpp -- the C ABI declared in include/pa.h: argument validation (pure host code,
+// run before any HIP call), launch configuration, workspace sizing and status reporting.
+// Kernels are enqueued through the launchers in pa_decode.hip and pa_cache.hip.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+int32_t g_partition_override = 0;   // 0 = automatic
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int32_t ok() {
+    g_last_error.clear();
+    return PA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+
+int32_t elt_bytes(int32_t kv_dtype) { return kv_dtype == PA_BF16 ? 2 : (kv_dtype == PA_F32 ? 4 : 0); }
+
+int32_t partition_tokens(int32_t block_size, int32_t max_blocks) {
+    if (g_partition_override > 0) return g_partition_override;
+    const int64_t cap = (int64_t)block_size * max_blocks;
+    if (cap <= pa_internal::kDefaultPartTokens) {
+        // one partition covers every sequence: round the capacity up to 64 tokens
+        int64_t p = (cap + 63) / 64 * 64;
+        return (int32_t)(p < 64 ? 64 : p);
+    }
+    return pa_internal::kDefaultPartTokens;
+}
+
+int32_t n_parts_for(int32_t block_size, int32_t max_blocks) {
+    const int64_t cap = (int64_t)block_size * max_blocks;
+    const int32_t P = partition_tokens(block_size, max_blocks);
+    const int64_t n = (cap + P - 1) / P;
+    return (int32_t)(n < 1 ? 1 : n);
+}
+
+size_t workspace_layout(int32_t B, int32_t Hq, int32_t D, int32_t n_parts, size_t* ml_offset) {
+    if (n_parts <= 1) {
+        *ml_offset = 0;
+        return 0;
+    }
+    const size_t rows = (size_t)B * (size_t)Hq * (size_t)n_parts;
+    const size_t o_bytes = rows * (size_t)D * sizeof(float);
+    const size_t off = (o_bytes + 255) / 256 * 256;
+    *ml_offset = off;
+    return off + rows * 2 * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int32_t status) {
+    switch (status) {
+        case PA_OK: return "PA_OK";
+        case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+        case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+        case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS";
+        case PA_ERR_HIP: return "PA_ERR_HIP";
+        default: return "PA_ERR_UNKNOWN";
+    }
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+int32_t pa_set_partition_tokens(int32_t tokens) {
+    if (tokens != 0 && (tokens < 64 || tokens > pa_internal::kMaxPartTokens || tokens % 64 != 0))
+        return fail(PA_ERR_INVALID_ARG, "partition tokens must be 0 or a multiple of 64 in [64, %d], got %d",
+                    pa_internal::kMaxPartTokens, tokens);
+    g_partition_override = tokens;
+    return ok();
+}
+
+int32_t pa_decode_partition_tokens(int32_t block_size, int32_t max_blocks) {
+    return partition_tokens(block_size, max_blocks);
+}
+
+size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t block_size,
+                                 int32_t max_blocks) {
+    if (B <= 0 || Hq <= 0 || D <= 0 || block_size <= 0 || max_blocks <= 0) return 0;
+    size_t ml;
+    return workspace_layout(B, Hq, D, n_parts_for(block_size, max_blocks), &ml);
+}
+
+int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                  int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                  int32_t max_blocks, float scale, int32_t kv_dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0 ||
+        max_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG,
+                    "pa_decode: bad sizes B=%d Hq=%d Hkv=%d D=%d block_size=%d num_blocks=%d max_blocks=%d",
+                    B, Hq, Hkv, D, block_size, num_blocks, max_blocks);
+    if (Hq % Hkv != 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (elt_bytes(kv_dtype) == 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode: kv_dtype %d is neither PA_F32 nor PA_BF16", kv_dtype);
+    if ((int64_t)block_size * max_blocks > (int64_t)1 << 30)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode: max_blocks * block_size exceeds 2^30");
+    if (B > 65535)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: B=%d exceeds 65535", B);
+    const int32_t G = Hq / Hkv;
+    if (D != 64 && D != 128)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d not built (64, 128)", D);
+    if (block_size != 16 && block_size != 32 && block_size != 64)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d not built (16, 32, 64)", block_size);
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: %d query heads per KV head not built (1, 2, 4, 8)", G);
+    if (Hkv > 65535)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: Hkv=%d exceeds 65535", Hkv);
+    if (B == 0) return ok();
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode: null pointer argument");
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+        return fail(PA_ERR_INVALID_ARG, "pa_decode: misaligned pointer (q/out/caches need 16 bytes)");
+    if ((int64_t)num_blocks * Hkv * block_size * D * elt_bytes(kv_dtype) < 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode: cache size overflows");
+    const int32_t P = partition_tokens(block_size, max_blocks);
+    if (P % block_size != 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode: partition %d not a multiple of block_size %d", P, block_size);
+    const int32_t n_parts = n_parts_for(block_size, max_blocks);
+    size_t ml_off = 0;
+    const size_t need = workspace_layout(B, Hq, D, n_parts, &ml_off);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(PA_ERR_INVALID_ARG, "pa_decode: workspace of %zu bytes needed, %zu given",
+                        need, workspace ? workspace_bytes : (size_t)0);
+        if (!aligned(workspace, 256))
+            return fail(PA_ERR_INVALID_ARG, "pa_decode: workspace must be 256-byte aligned");
+    }
+    if (n_parts > 0x7fffffff / 2)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: too many partitions");
+
+    pa_internal::DecodeLaunch a;
+    a.out = out;
+    a.ws_o = need ? static_cast<float*>(workspace) : nullptr;
+    a.ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_off) : nullptr;
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.tables = block_tables;
+    a.lens = seq_lens;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.bs = block_size;
+    a.num_blocks = num_blocks;
+    a.max_blocks = max_blocks;
+    a.part_tokens = P;
+    a.n_parts = n_parts;
+    a.kv_dtype = kv_dtype;
+    a.scale = scale;
+    a.stream = stream;
+    const char* err = "";
+    const int e = pa_internal::launch_decode(a, &err);
+    if (e != 0) return fail(PA_ERR_HIP, "pa_decode: launch failed: %s (%d)", err, e);
+    return ok();
+}
+
+int32_t pa_reshape_and_cache(void* k_cache, void* v_cache, const void* key, const void* value,
+                             const int32_t* slot_mapping, int32_t T, int32_t Hkv, int32_t D,
+                             int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                             void* stream) {
+    const int32_t eb = elt_bytes(kv_dtype);
+    if (eb == 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_reshape_and_cache: kv_dtype %d is neither PA_F32 nor PA_BF16", kv_dtype);
+    if (T < 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_reshape_and_cache: bad sizes T=%d Hkv=%d D=%d block_size=%d num_blocks=%d",
+                    T, Hkv, D, block_size, num_blocks);
+    if ((D * eb) % 16 != 0 || D > 512)
+        return fail(PA_ERR_UNSUPPORTED, "pa_reshape_and_cache: head_dim %d (rows must be whole 16-byte units, <= 512)", D);
+    if ((int64_t)num_blocks * block_size > 0x7fffffff)
+        return fail(PA_ERR_UNSUPPORTED, "pa_reshape_and_cache: more than 2^31 slots");
+    if (T == 0) return ok();
+    if (!k_cache || !v_cache || !key || !value || !slot_mapping)
+        return fail(PA_ERR_INVALID_ARG, "pa_reshape_and_cache: null pointer argument");
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(key, 16) || !aligned(value, 16) ||
+        !aligned(slot_mapping, 4))
+        return fail(PA_ERR_INVALID_ARG, "pa_reshape_and_cache: misaligned pointer");
+    const char* err = "";
+    const int e = pa_internal::launch_reshape_and_cache(k_cache, v_cache, key, value, slot_mapping,
+                                                        T, Hkv, D * eb, block_size, num_blocks,
+                                                        stream, &err);
+    if (e != 0) return fail(PA_ERR_HIP, "pa_reshape_and_cache: launch failed: %s (%d)", err, e);
+    return ok();
+}
+
+int32_t pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t N,
+                       int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                       int32_t kv_dtype, void* stream) {
+    const int32_t eb = elt_bytes(kv_dtype);
+    if (eb == 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: kv_dtype %d is neither PA_F32 nor PA_BF16", kv_dtype);
+    if (N < 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: bad sizes N=%d Hkv=%d D=%d block_size=%d num_blocks=%d",
+                    N, Hkv, D, block_size, num_blocks);
+    const int64_t block_bytes = (int64_t)Hkv * block_size * D * eb;
+    if (block_bytes % 16 != 0)
+        return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: block of %lld bytes is not a whole number of 16-byte units",
+                    (long long)block_bytes);
+    if (N == 0) return ok();
+    if (!k_cache || !v_cache || !block_pairs)
+        return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: null pointer argument");
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_pairs, 4))
+        return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: misaligned pointer");
+    const char* err = "";
+    const int e = pa_internal::launch_copy_blocks(k_cache, v_cache, block_pairs, N, block_bytes,
+                                                  num_blocks, stream, &err);
+    if (e != 0) return fail(PA_ERR_HIP, "pa_copy_blocks: launch failed: %s (%d)", err, e);
+    return ok();
+}
+
+}  // extern "C"
+
+namespace pa_internal {
+// The allocator entry points (allocator.cpp) report through the same thread-local message.
+int32_t set_error(int32_t status, const char* msg) { return fail(status, "%s", msg); }
+int32_t clear_error() { return ok(); }
+}  // namespace pa_internal

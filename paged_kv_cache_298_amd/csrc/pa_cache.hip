@@ -1,0 +1,126 @@
+// pa_cache.hip -- the two small kernels that feed paged decode attention on gfx950.
+//
+// reshape_and_cache: write each new token's K and V row of every KV head to its physical
+//   slot s, i.e. block s / block_size, offset s % block_size. The slot is the flat index
+//   of [P2] "Paged Attention" tutorial (infra.pidoku.co.in), section 4 "Tiny example",
+//   PhysicalIndex: table[pos / block_size] * block_size + pos % block_size.
+// copy_blocks: clone whole physical blocks (K and V, all heads and slots) before a write
+//   into a shared block, the copy-on-write of [P2] section 5 "Copy-on-write sharing" and
+//   [P4] "PagedAttention & KV-Cache Management in High-Throughput LLM Serving"
+//   (subroutine-cs.cc), section 3.
+// Both are bit copies moved in 16-byte units, one unit per lane per access, consecutive
+// lanes on consecutive units, so every wave-wide access is 1 KiB of contiguous bytes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// One thread per 16-byte unit of a (token, KV head) row; K and V moved together.
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    u32x4_t* __restrict__ kc, u32x4_t* __restrict__ vc, const u32x4_t* __restrict__ key,
+    const u32x4_t* __restrict__ value, const int32_t* __restrict__ slots, int64_t total,
+    int Hkv, int row_units, int bs, int64_t nslots) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int c = (int)(idx % row_units);
+    const int64_t r = idx / row_units;     // token * Hkv + head
+    const int g = (int)(r % Hkv);
+    const int64_t i = r / Hkv;
+    const int s = slots[i];
+    if (s < 0 || (int64_t)s >= nslots) return;
+    const int64_t blk = s / bs;
+    const int64_t off = s % bs;
+    const int64_t dst = ((blk * Hkv + g) * bs + off) * row_units + c;
+    const u32x4_t kx = key[idx];
+    const u32x4_t vx = value[idx];
+    kc[dst] = kx;
+    vc[dst] = vx;
+}
+
+constexpr int kCopyUnitsPerThread = 4;
+
+// blockIdx.y = pair index; each block moves 256 * 4 units (16 KiB) of K and of V.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4_t* __restrict__ kc,
+                                                          u32x4_t* __restrict__ vc,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int64_t block_units, int num_blocks) {
+    const int n = blockIdx.y;
+    const int src = pairs[2 * n];
+    const int dst = pairs[2 * n + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+    const int64_t base = (int64_t)blockIdx.x * (256 * kCopyUnitsPerThread) + threadIdx.x;
+    const u32x4_t* ks = kc + (int64_t)src * block_units;
+    const u32x4_t* vs = vc + (int64_t)src * block_units;
+    u32x4_t* kd = kc + (int64_t)dst * block_units;
+    u32x4_t* vd = vc + (int64_t)dst * block_units;
+    u32x4_t kx[kCopyUnitsPerThread], vx[kCopyUnitsPerThread];
+#pragma unroll
+    for (int j = 0; j < kCopyUnitsPerThread; ++j) {
+        const int64_t u = base + j * 256;
+        if (u < block_units) {
+            kx[j] = ks[u];
+            vx[j] = vs[u];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kCopyUnitsPerThread; ++j) {
+        const int64_t u = base + j * 256;
+        if (u < block_units) {
+            kd[u] = kx[j];
+            vd[u] = vx[j];
+        }
+    }
+}
+
+}  // namespace
+
+namespace pa_internal {
+
+int launch_reshape_and_cache(void* k_cache, void* v_cache, const void* key, const void* value,
+                             const int32_t* slot_mapping, int32_t T, int32_t Hkv,
+                             int32_t row_bytes, int32_t block_size, int32_t num_blocks,
+                             void* stream, const char** err) {
+    if (T == 0) return 0;
+    const int row_units = row_bytes / 16;
+    const int64_t total = (int64_t)T * Hkv * row_units;
+    const int64_t grid = (total + 255) / 256;
+    hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)grid), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), static_cast<u32x4_t*>(k_cache),
+                       static_cast<u32x4_t*>(v_cache), static_cast<const u32x4_t*>(key),
+                       static_cast<const u32x4_t*>(value), slot_mapping, total, (int)Hkv,
+                       row_units, (int)block_size, (int64_t)num_blocks * block_size);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        *err = hipGetErrorString(e);
+        return (int)e;
+    }
+    return 0;
+}
+
+int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t N,
+                       int64_t block_bytes, int32_t num_blocks, void* stream, const char** err) {
+    if (N == 0) return 0;
+    const int64_t units = block_bytes / 16;
+    const int64_t per_block = 256 * kCopyUnitsPerThread;
+    const int64_t gx = (units + per_block - 1) / per_block;
+    constexpr int32_t kMaxGridY = 65535;
+    for (int32_t first = 0; first < N; first += kMaxGridY) {
+        const int32_t n = N - first < kMaxGridY ? N - first : kMaxGridY;
+        hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)n), dim3(256), 0,
+                           reinterpret_cast<hipStream_t>(stream), static_cast<u32x4_t*>(k_cache),
+                           static_cast<u32x4_t*>(v_cache), block_pairs + 2 * (int64_t)first,
+                           units, (int)num_blocks);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        *err = hipGetErrorString(e);
+        return (int)e;
+    }
+    return 0;
+}
+
+}  // namespace pa_internal

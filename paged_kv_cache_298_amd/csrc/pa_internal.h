@@ -1,0 +1,44 @@
+// pa_internal.h -- declarations shared by the C-ABI layer (plain C++) and the HIP kernel
+// launchers. No HIP types appear here, so the ABI layer builds with any C++ compiler.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa_internal {
+
+// Everything one pa_decode call needs, already validated on the host.
+struct DecodeLaunch {
+    float* out;              // [B, Hq, D]
+    float* ws_o;             // [B, Hq, n_parts, D]  (unused when n_parts == 1)
+    float* ws_ml;            // [B, Hq, n_parts, 2]  (running max in log2 units, sum)
+    const void* q;           // [B, Hq, D]
+    const void* k;           // [num_blocks, Hkv, bs, D]
+    const void* v;
+    const int32_t* tables;   // [B, max_blocks]
+    const int32_t* lens;     // [B]
+    int32_t B, Hq, Hkv, D, bs, num_blocks, max_blocks;
+    int32_t part_tokens;     // tokens per partition (multiple of 64, <= kMaxPartTokens)
+    int32_t n_parts;         // ceil(max_blocks * bs / part_tokens)
+    int32_t kv_dtype;        // PA_F32 / PA_BF16
+    float scale;
+    void* stream;
+};
+
+constexpr int kMaxPartTokens = 1024;
+constexpr int kDefaultPartTokens = 256;
+
+// Each returns 0 on success or a nonzero HIP error code (message in *err).
+int launch_decode(const DecodeLaunch& a, const char** err);
+int launch_reshape_and_cache(void* k_cache, void* v_cache, const void* key, const void* value,
+                             const int32_t* slot_mapping, int32_t T, int32_t Hkv,
+                             int32_t row_bytes, int32_t block_size, int32_t num_blocks,
+                             void* stream, const char** err);
+int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t N,
+                       int64_t block_bytes, int32_t num_blocks, void* stream, const char** err);
+
+// Thread-local error message of the C ABI (pa_last_error); set_error returns status.
+int32_t set_error(int32_t status, const char* msg);
+int32_t clear_error();
+
+}  // namespace pa_internal

@@ -1,0 +1,215 @@
+"""ctypes binding of libpa.so (include/pa.h), with the C names.
+
+Argument marshalling only: tensors are passed by data pointer with their shapes, the
+current HIP stream of their device is used unless one is given, and a non-zero status is
+raised as PaError carrying pa_last_error(). Every step of the hot path runs in libpa's
+kernels; there is no fallback. Importing this module raises if libpa.so is missing.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} not found: build it with __graft_entry__.build() "
+                      "(or python paged_kv_cache_298_amd/build.py)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+PA_F32, PA_BF16 = 0, 1
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS, PA_ERR_HIP = 0, -1, -2, -3, -4
+
+_vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_P32 = ctypes.POINTER(ctypes.c_int32)
+
+_SIGS = {
+    "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                         _f32, _i32, _vp, _sz, _vp]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_partition_tokens": (_i32, [_i32, _i32]),
+    "pa_set_partition_tokens": (_i32, [_i32]),
+    "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                    _vp]),
+    "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_status_string": (ctypes.c_char_p, [_i32]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_abi_version": (_i32, []),
+    "pa_alloc_create": (_vp, [_i32, _i32, _vp]),
+    "pa_alloc_destroy": (None, [_vp]),
+    "pa_alloc_allocate": (_i32, [_vp, _i32, _vp]),
+    "pa_alloc_free": (_i32, [_vp, _vp, _i32]),
+    "pa_alloc_fork": (_i32, [_vp, _vp, _i32, _vp]),
+    "pa_alloc_append_token": (_i32, [_vp, _vp, _P32, _i32, _P32, _P32, _P32, _P32]),
+    "pa_alloc_refcount": (_i32, [_vp, _i32]),
+    "pa_alloc_num_free": (_i32, [_vp]),
+    "pa_alloc_free_list": (_i32, [_vp, _vp, _i32]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTS = tuple(_SIGS)
+
+
+class PaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_lib.pa_status_string(status).decode()}: {message}")
+        self.status = status
+
+
+def _check(status):
+    if status != PA_OK:
+        raise PaError(status, _lib.pa_last_error().decode())
+    return status
+
+
+def _kv_dtype(t):
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype == torch.float32:
+        return PA_F32
+    raise TypeError(f"element type must be torch.bfloat16 or torch.float32, got {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    if t.is_cuda:
+        return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return ctypes.c_void_p(0)
+
+
+def abi_version():
+    return int(_lib.pa_abi_version())
+
+
+def pa_decode_workspace_bytes(B, Hq, D, block_size, max_blocks):
+    return int(_lib.pa_decode_workspace_bytes(B, Hq, D, block_size, max_blocks))
+
+
+def pa_decode_partition_tokens(block_size, max_blocks):
+    return int(_lib.pa_decode_partition_tokens(block_size, max_blocks))
+
+
+def pa_set_partition_tokens(tokens):
+    _check(_lib.pa_set_partition_tokens(int(tokens)))
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, workspace=None,
+              stream=None):
+    """out [B, Hq, D] fp32 <- paged decode attention. k_cache/v_cache are
+    [num_blocks, Hkv, block_size, D]; block_tables int32 [B, max_blocks]; seq_lens int32 [B].
+    workspace: a uint8 tensor of at least pa_decode_workspace_bytes(...) bytes (allocated
+    here, on q's device, when None and needed)."""
+    B, Hq, D = q.shape
+    nb, Hkv, bs, _ = k_cache.shape
+    max_blocks = block_tables.shape[1]
+    need = pa_decode_workspace_bytes(B, Hq, D, bs, max_blocks)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                          _ptr(seq_lens), B, Hq, Hkv, D, bs, nb, max_blocks, float(scale),
+                          _kv_dtype(k_cache), _ptr(workspace), ws_bytes, _stream(q, stream)))
+    return out
+
+
+def pa_reshape_and_cache(k_cache, v_cache, key, value, slot_mapping, stream=None):
+    """Write key/value [T, Hkv, D] into the caches at slot_mapping int32 [T] (s < 0 skips)."""
+    nb, Hkv, bs, D = k_cache.shape
+    T = slot_mapping.shape[0]
+    _check(_lib.pa_reshape_and_cache(_ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value),
+                                     _ptr(slot_mapping), T, Hkv, D, bs, nb, _kv_dtype(k_cache),
+                                     _stream(k_cache, stream)))
+
+
+def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None):
+    """Copy whole blocks src -> dst for each row of block_pairs int32 [N, 2]."""
+    nb, Hkv, bs, D = k_cache.shape
+    N = block_pairs.shape[0]
+    _check(_lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs), N, Hkv, D, bs, nb,
+                               _kv_dtype(k_cache), _stream(k_cache, stream)))
+
+
+class BlockAllocator:
+    """The host refcounted block allocator (pa_alloc_*). Block ids and tables are plain
+    Python lists / int32 numpy arrays; nothing here touches the GPU."""
+
+    def __init__(self, num_blocks, block_size, initial_free_order=None):
+        import numpy as np
+        self._np = np
+        self.block_size = int(block_size)
+        self.num_blocks = int(num_blocks)
+        arr = None
+        if initial_free_order is not None:
+            arr = np.ascontiguousarray(initial_free_order, dtype=np.int32)
+            if arr.shape != (self.num_blocks,):
+                raise ValueError("initial_free_order must list every block id once")
+        h = _lib.pa_alloc_create(self.num_blocks, self.block_size,
+                                 arr.ctypes.data_as(_vp) if arr is not None else None)
+        if not h:
+            raise PaError(PA_ERR_INVALID_ARG, _lib.pa_last_error().decode())
+        self._h = ctypes.c_void_p(h)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            _lib.pa_alloc_destroy(h)
+            self._h = None
+
+    def _arr(self, xs):
+        return self._np.ascontiguousarray(xs, dtype=self._np.int32)
+
+    def allocate(self, n):
+        out = self._np.zeros(max(int(n), 1), dtype=self._np.int32)
+        _check(_lib.pa_alloc_allocate(self._h, int(n), out.ctypes.data_as(_vp)))
+        return [int(x) for x in out[:int(n)]]
+
+    def free(self, blocks):
+        a = self._arr(blocks)
+        _check(_lib.pa_alloc_free(self._h, a.ctypes.data_as(_vp), a.shape[0]))
+
+    def fork(self, blocks):
+        a = self._arr(blocks)
+        out = self._np.zeros(max(a.shape[0], 1), dtype=self._np.int32)
+        _check(_lib.pa_alloc_fork(self._h, a.ctypes.data_as(_vp), a.shape[0],
+                                  out.ctypes.data_as(_vp)))
+        return [int(x) for x in out[:a.shape[0]]]
+
+    def append_token(self, table, seq_len, table_cap=None):
+        """table: list of block ids (updated in place). Returns (new_len, slot, cow) with cow
+        None or (src, dst)."""
+        cap = int(table_cap) if table_cap is not None else len(table) + 1
+        buf = self._np.zeros(max(cap, len(table), 1), dtype=self._np.int32)
+        buf[:len(table)] = table
+        n = ctypes.c_int32(len(table))
+        L = ctypes.c_int32(int(seq_len))
+        slot, src, dst = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.pa_alloc_append_token(self._h, buf.ctypes.data_as(_vp), ctypes.byref(n), cap,
+                                          ctypes.byref(L), ctypes.byref(slot), ctypes.byref(src),
+                                          ctypes.byref(dst)))
+        table[:] = [int(x) for x in buf[:n.value]]
+        cow = None if src.value < 0 else (src.value, dst.value)
+        return L.value, slot.value, cow
+
+    def refcount(self, block):
+        r = _lib.pa_alloc_refcount(self._h, int(block))
+        return _check(r) if r < 0 else int(r)
+
+    def num_free(self):
+        return int(_lib.pa_alloc_num_free(self._h))
+
+    def free_list(self):
+        out = self._np.zeros(max(self.num_blocks, 1), dtype=self._np.int32)
+        n = _lib.pa_alloc_free_list(self._h, out.ctypes.data_as(_vp), self.num_blocks)
+        return [int(x) for x in out[:n]]

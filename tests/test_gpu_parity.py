@@ -1,0 +1,271 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, on an MI355X.
+
+Attention: max-abs error over every output element <= 1e-5 (fp32 caches) or 2e-2 (bf16
+caches, fp32 accumulation). Cache write and block copy: bit-exact over the whole cache.
+Invariants (placement, sharing, poison, determinism) are checked bit for bit on the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_298_amd import workloads as W
+from tests._gpu_helpers import (DEV, TOL, DevWorkload, gpu_step, max_err, note, oracle_step,
+                                to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_cache_298_amd import pa as _pa
+    _pa.pa_set_partition_tokens(0)
+    return _pa
+
+
+def _parity(pa, oracle, wl, rows=None, tag=""):
+    note(f"{wl.name} {tag} B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} bs={wl.block_size} "
+         f"dtype={wl.dtype} lens[:8]={list(wl.seq_lens[:8])}")
+    dw = DevWorkload(wl)
+    got = gpu_step(pa, dw)
+    ref, kc, vc = oracle_step(oracle, wl, rows=rows)
+    if rows is not None:
+        got = got.reshape(wl.B * wl.Hq, wl.D)[rows]
+    err = max_err(got, ref)
+    note(f"  max abs err {err:.3e} (tol {TOL[wl.dtype]})")
+    assert err <= TOL[wl.dtype]
+    return dw, kc, vc
+
+
+def test_config1_tiny_fp32(pa, oracle):
+    wl = W.config(1)
+    dw, kc, vc = _parity(pa, oracle, wl)
+    assert np.array_equal(to_host(dw.k).view(np.uint32), kc.view(np.uint32))
+    assert np.array_equal(to_host(dw.v).view(np.uint32), vc.view(np.uint32))
+
+
+SMALL = [
+    # B, Hq, Hkv, D, bs, dtype, lens
+    (4, 8, 2, 128, 16, W.BF16, [1, 15, 16, 17]),
+    (5, 32, 8, 128, 16, W.BF16, [255, 256, 257, 513, 700]),
+    (3, 16, 2, 128, 32, W.BF16, [31, 32, 1000]),
+    (3, 8, 8, 64, 64, W.BF16, [63, 64, 65]),
+    (4, 16, 2, 64, 16, W.BF16, [2, 100, 300, 1500]),
+    (2, 4, 2, 128, 64, W.BF16, [3000, 129]),
+    (3, 8, 4, 128, 16, W.F32, [1, 40, 600]),
+    (3, 8, 1, 64, 32, W.F32, [5, 64, 333]),
+    (2, 2, 2, 128, 64, W.F32, [70, 1]),
+    (4, 4, 4, 64, 16, W.F32, [16, 17, 255, 1024]),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"G{c[1] // c[2]}-D{c[3]}-bs{c[4]}-{c[5]}")
+def test_small_shapes(pa, oracle, case):
+    B, Hq, Hkv, D, bs, dt, lens = case
+    wl = W.make_workload("small", B, Hq, Hkv, D, bs, lens, dt, seed=sum(lens) + D)
+    _parity(pa, oracle, wl)
+
+
+@pytest.mark.parametrize("L", [1, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 512, 513])
+def test_edge_lengths(pa, oracle, L):
+    wl = W.make_workload("edge", 2, 32, 8, 128, 16, [L, max(1, L // 2)], W.BF16, seed=L,
+                         max_blocks=64)
+    _parity(pa, oracle, wl, tag=f"L={L}")
+
+
+def test_empty_sequences_give_zero_rows(pa, oracle):
+    wl = W.make_workload("empty", 4, 8, 2, 128, 16, [0, 37, 0, 300], W.BF16, seed=3,
+                         max_blocks=32)
+    dw, _, _ = _parity(pa, oracle, wl)
+    out = dw.out.cpu().numpy()
+    assert np.array_equal(out[0], np.zeros_like(out[0]))
+    assert np.array_equal(out[2], np.zeros_like(out[2]))
+
+
+def test_config2_llama8b_full(pa, oracle):
+    _parity(pa, oracle, W.config(2))
+
+
+def test_config3_shared_prefix_full(pa, oracle):
+    wl = W.config(3)
+    dw, kc, vc = _parity(pa, oracle, wl)
+    # the clones and the written slots are bit-exact over the whole cache
+    assert np.array_equal(to_host(dw.k), kc)
+    assert np.array_equal(to_host(dw.v), vc)
+
+
+def test_config4_llama70b_full(pa, oracle):
+    _parity(pa, oracle, W.config(4))
+
+
+def test_config5_long_context_sampled(pa, oracle):
+    wl = W.config(5)
+    rng = np.random.default_rng(5)
+    rows = sorted(set([2 * 32 + h for h in range(32)] +
+                      [int(x) for x in rng.choice(wl.B * wl.Hq, 24, replace=False)]))
+    _parity(pa, oracle, wl, rows=np.array(rows, np.int32), tag="rows")
+
+
+def test_cow_through_the_append_path(pa, oracle):
+    """A prompt that ends inside a block (2040 tokens, bs 16) forked 4 ways; each fork
+    appends one token through the reference block manager: three clone the shared last
+    block (copy old -> new), the last writes in place."""
+    from oracle.block_manager import BlockManager, Sequence
+    bs, prompt, nf = 16, 2040, 4
+    base = W.make_workload("cow", 1, 32, 8, 128, bs, [prompt], W.BF16, seed=77, max_blocks=160,
+                           num_blocks=200, keep_logical=True)
+    mgr = BlockManager(base.num_blocks, bs,
+                       initial_free=[int(x) for x in np.random.default_rng(1).permutation(base.num_blocks)])
+    root = Sequence(mgr, prompt)
+    seqs = [root] + [root.fork() for _ in range(nf - 1)]
+    rng = np.random.default_rng(2)
+    k = np.full_like(base.k_cache, W.NAN_BF16)
+    v = np.full_like(base.v_cache, W.NAN_BF16)
+    for t in range(prompt):   # the shared prompt, in the manager's blocks
+        k[root.table[t // bs], :, t % bs] = base.logical_k[0][t]
+        v[root.table[t // bs], :, t % bs] = base.logical_v[0][t]
+    pairs, slots = [], []
+    for s in seqs:
+        slot, cow = s.append_token()
+        slots.append(slot)
+        if cow:
+            pairs.append(cow)
+    assert len(pairs) == nf - 1
+    tables = np.zeros((nf, 160), np.int32)
+    for i, s in enumerate(seqs):
+        tables[i, :len(s.table)] = s.table
+    nk = W.bf16_from_f32(rng.standard_normal((nf, 8, 128), dtype=np.float32))
+    nv = W.bf16_from_f32(rng.standard_normal((nf, 8, 128), dtype=np.float32))
+    q = W.bf16_from_f32(rng.standard_normal((nf, 32, 128), dtype=np.float32))
+    wl = W.Workload(name="cow", dtype=W.BF16, B=nf, Hq=32, Hkv=8, D=128, block_size=bs,
+                    num_blocks=base.num_blocks, max_blocks=160, scale=base.scale, q=q,
+                    k_cache=k, v_cache=v, block_tables=tables,
+                    seq_lens=np.full(nf, prompt + 1, np.int32), new_key=nk, new_value=nv,
+                    slot_mapping=np.array(slots, np.int32),
+                    cow_pairs=np.array(pairs, np.int32))
+    dw, kc, vc = _parity(pa, oracle, wl)
+    assert np.array_equal(to_host(dw.k), kc) and np.array_equal(to_host(dw.v), vc)
+
+
+# ------------------------------------------------------------------ bit-exact kernels
+
+def test_reshape_and_cache_every_token_of_config2_bit_exact(pa, oracle):
+    wl = W.config(2, keep_logical=True)
+    bs = wl.block_size
+    slots, keys, vals = [], [], []
+    for b in range(wl.B):
+        L = int(wl.seq_lens[b])
+        t = np.arange(L)
+        slots.append(wl.block_tables[b, t // bs] * bs + t % bs)
+        keys.append(wl.logical_k[b])
+        vals.append(wl.logical_v[b])
+    slots = np.concatenate(slots).astype(np.int32)
+    order = np.random.default_rng(0).permutation(len(slots))
+    slots, keys, vals = slots[order], np.concatenate(keys)[order], np.concatenate(vals)[order]
+    slots[::97] = -1                                   # padding entries are skipped
+    empty = np.full_like(wl.k_cache, W.NAN_BF16)
+    note(f"reshape_and_cache T={len(slots)}")
+    kd, vd = (torch.from_numpy(empty.view(np.int16)).view(torch.bfloat16).to(DEV) for _ in range(2))
+    from tests._gpu_helpers import to_dev
+    pa.pa_reshape_and_cache(kd, vd, to_dev(keys), to_dev(vals), to_dev(slots))
+    torch.cuda.synchronize()
+    kr, vr = oracle.reshape_and_cache(empty, empty, keys, vals, slots)
+    assert np.array_equal(to_host(kd), kr)
+    assert np.array_equal(to_host(vd), vr)
+
+
+def test_copy_blocks_bit_exact_fp32(pa, oracle):
+    rng = np.random.default_rng(8)
+    kc = rng.standard_normal((300, 4, 32, 64)).astype(np.float32)
+    vc = rng.standard_normal((300, 4, 32, 64)).astype(np.float32)
+    src = rng.choice(150, 90, replace=False)
+    dst = 150 + rng.choice(150, 90, replace=False)
+    pairs = np.stack([src, dst], 1).astype(np.int32)
+    from tests._gpu_helpers import to_dev
+    note("copy_blocks fp32 90 pairs")
+    kd, vd = to_dev(kc), to_dev(vc)
+    pa.pa_copy_blocks(kd, vd, to_dev(pairs))
+    torch.cuda.synchronize()
+    kr, vr = oracle.copy_blocks(kc, vc, pairs)
+    assert np.array_equal(to_host(kd).view(np.uint32), kr.view(np.uint32))
+    assert np.array_equal(to_host(vd).view(np.uint32), vr.view(np.uint32))
+
+
+# ------------------------------------------------------------------ invariants (bitwise)
+
+def test_placement_does_not_change_a_bit(pa):
+    outs = []
+    for placement in ("permute", "identity", "reversed"):
+        wl = W.make_workload("perm", 6, 32, 8, 128, 16, [5, 300, 1024, 17, 2000, 64], W.BF16,
+                             seed=44, placement=placement)
+        note(f"placement {placement}")
+        outs.append(gpu_step(pa, DevWorkload(wl)))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_poison_does_not_change_a_bit(pa):
+    outs = []
+    for poison in (True, False):
+        wl = W.make_workload("poison", 5, 32, 8, 128, 32, [1, 31, 33, 700, 4000], W.BF16,
+                             seed=12, poison=poison)
+        note(f"poison {poison}")
+        o = gpu_step(pa, DevWorkload(wl))
+        assert np.isfinite(o).all()
+        outs.append(o)
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_shared_prefix_equals_private_copies_bitwise(pa):
+    wl = W.make_shared_prefix("s", 2, 4, 512, 40, 32, 8, 128, 16, W.BF16, seed=19,
+                              keep_logical=True)
+    note("shared prefix")
+    shared = gpu_step(pa, DevWorkload(wl))
+    priv = W.make_workload("p", wl.B, wl.Hq, wl.Hkv, wl.D, 16, wl.seq_lens, W.BF16, seed=1,
+                           keep_logical=True)
+    priv.q[:] = wl.q
+    for b in range(wl.B):
+        L = int(wl.seq_lens[b])
+        for t in range(L - 1):
+            blk = priv.block_tables[b, t // 16]
+            priv.k_cache[blk, :, t % 16] = wl.logical_k[b][t]
+            priv.v_cache[blk, :, t % 16] = wl.logical_v[b][t]
+        priv.new_key[b] = wl.logical_k[b][L - 1]
+        priv.new_value[b] = wl.logical_v[b][L - 1]
+    note("private copies")
+    private = gpu_step(pa, DevWorkload(priv))
+    assert np.array_equal(shared, private)
+
+
+def test_repeated_calls_are_bitwise_equal(pa):
+    wl = W.config(4)
+    dw = DevWorkload(wl)
+    note("determinism cfg4")
+    a = gpu_step(pa, dw).copy()
+    for _ in range(3):
+        pa.pa_decode(dw.out, dw.q, dw.k, dw.v, dw.bt, dw.sl, wl.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(a, dw.out.cpu().numpy())
+
+
+@pytest.mark.parametrize("P", [64, 128, 512, 1024])
+def test_partition_length_changes_only_rounding(pa, oracle, P):
+    wl = W.make_workload("split", 4, 32, 8, 128, 64, [100, 1023, 1025, 4000], W.BF16, seed=P,
+                         max_blocks=64)
+    pa.pa_set_partition_tokens(P)
+    try:
+        _parity(pa, oracle, wl, tag=f"P={P}")
+    finally:
+        pa.pa_set_partition_tokens(0)
+
+
+def test_one_token_returns_its_value_exactly(pa):
+    for dt in (W.F32, W.BF16):
+        wl = W.make_workload("one", 3, 8, 2, 128, 16, [1, 1, 1], dt, seed=5, keep_logical=True)
+        note(f"one token {dt}")
+        out = gpu_step(pa, DevWorkload(wl))
+        for b in range(3):
+            v = wl.logical_v[b][0]
+            v = W.bf16_to_f32(v) if dt == W.BF16 else v
+            for h in range(8):
+                assert np.array_equal(out[b, h], v[h // 4])
