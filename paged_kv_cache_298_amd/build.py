@@ -20,7 +20,7 @@ HIP_SOURCES = ["pa_decode.hip", "pa_cache.hip"]
 HOST_SOURCES = ["pa_api.cpp", "allocator.cpp"]
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-munsafe-fp-atomics"]
+             "-munsafe-fp-atomics", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra"]
 
 

@@ -151,8 +151,9 @@ int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_
         if (!aligned(workspace, 256))
             return fail(PA_ERR_INVALID_ARG, "pa_decode: workspace must be 256-byte aligned");
     }
-    if (n_parts > 0x7fffffff / 2)
-        return fail(PA_ERR_UNSUPPORTED, "pa_decode: too many partitions");
+    if ((int64_t)n_parts * Hkv * B > 0x7fffffff)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: %lld work items exceed the grid limit",
+                    (long long)n_parts * Hkv * B);
 
     pa_internal::DecodeLaunch a;
     a.out = out;

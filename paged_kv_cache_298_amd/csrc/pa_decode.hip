@@ -50,7 +50,7 @@ struct Params {
     const char* v;
     const int32_t* tables;
     const int32_t* lens;
-    int Hq, Hkv, bs, bs_shift, num_blocks, max_blocks, part_tokens, n_parts;
+    int B, Hq, Hkv, bs, bs_shift, num_blocks, max_blocks, part_tokens, n_parts;
     float scale_log2;
 };
 
@@ -80,6 +80,43 @@ __device__ __forceinline__ f32x4_t qk_tile(const u32x4_t (&kf)[KL], const u32x4_
     return acc;
 }
 
+#ifndef PA_DECODE_NT
+#define PA_DECODE_NT 0
+#endif
+
+// K/V bytes are read once per call: stream them past the caches when PA_DECODE_NT is set.
+__device__ __forceinline__ u32x4_t load16(const u32x4_t* ptr) {
+#if PA_DECODE_NT
+    return __builtin_nontemporal_load(ptr);
+#else
+    return *ptr;
+#endif
+}
+
+// The workgroup is exactly one wavefront, so LDS traffic between its lanes needs only
+// ordering, not a workgroup barrier: LDS instructions of one wave execute in issue order.
+// Wavefront-scope fences keep the compiler from reordering across this point and, unlike
+// a workgroup barrier, do not wait for outstanding global loads.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Work item of this workgroup. The grid is one-dimensional and ordered KV head fastest,
+// then sequence, then partition. Consecutive workgroups are dealt round-robin to the
+// eight XCDs, each of which has its own L2 and its own link to HBM, so this order gives
+// every XCD the same mix of heads, sequences and partitions: with 8 KV heads, XCD k serves
+// KV head k of every partition, an exact eighth of the bytes. (Partition-fastest order
+// would send every sequence's first partition, the one that always exists, to one XCD.)
+__device__ __forceinline__ void work_item(const Params& p, int& g, int& b, int& part) {
+    const int id = blockIdx.x;
+    g = id % p.Hkv;
+    const int rest = id / p.Hkv;
+    b = rest % p.B;
+    part = rest / p.B;
+}
+
 template <int G>
 __device__ __forceinline__ void load_probs(const float* __restrict__ src, float (&p)[G]) {
     if constexpr (G % 4 == 0) {
@@ -97,26 +134,24 @@ __device__ __forceinline__ void load_probs(const float* __restrict__ src, float 
     }
 }
 
-template <bool BF16, int D, int G>
+template <bool BF16, int D, int G, int DEPTH>
 __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
     constexpr int EB = BF16 ? 2 : 4;   // bytes per element
     constexpr int E = 16 / EB;         // elements per 16-byte load
     constexpr int KQ = D / 4;          // elements of a K row fed by one lane (quarter row)
-    constexpr int KL = KQ / E;         // 16-byte loads per lane per 16-token K group
+    constexpr int NL = KQ / E;         // 16-byte loads per lane per 16-token group (K or V)
     constexpr int O = D / E;           // lanes covering one V row
     constexpr int R = 64 / O;          // V rows per wave-wide load
-    constexpr int VL = 16 / R;         // wave-wide V loads per 16-token group
     constexpr int ROW = D * EB;        // bytes per cached row
-    static_assert(KL >= 1 && R >= 1 && VL >= 1, "unsupported head size");
+    static_assert(NL >= 1 && R >= 1 && 16 / R == NL, "unsupported head size");
 
     extern __shared__ float smem[];
-    float* s_lds = smem;                                  // [part_tokens][G]
-    int* tbl = reinterpret_cast<int*>(smem + p.part_tokens * G);   // [part_tokens / 16]
+    float* s_lds = smem;                                            // [part_tokens][G]
+    int* tbl = reinterpret_cast<int*>(smem + p.part_tokens * G);    // [part_tokens / 16]
 
     const int lane = threadIdx.x;
-    const int part = blockIdx.x;
-    const int g = blockIdx.y;
-    const int b = blockIdx.z;
+    int g, b, part;
+    work_item(p, g, b, part);
     const int cap = p.max_blocks * p.bs;
     int L = p.lens[b];
     L = L < 0 ? 0 : (L > cap ? cap : L);
@@ -144,111 +179,135 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
         tbl[i] = e;
     }
 
-    // query fragment: lane (column h = lane % 16, quarter qd = lane / 16) holds
-    // q[b, hq0 + h, qd*KQ .. qd*KQ + KQ); zero for padded columns h >= G
+    // Head-dim split of the QK contraction: MFMA step c takes elements
+    // [c*4E, c*4E + 4E) of every row, lane quarter qd = lane / 16 the E of them at
+    // c*4E + qd*E. Any split that A and B share gives the same dot products; this one makes
+    // every K load instruction read 64 contiguous bytes of each of the 16 rows.
+    // Query fragment: lane (column h = lane % 16, quarter qd) holds those elements of
+    // q[b, hq0 + h, :]; zero for padded columns h >= G.
     const int col = lane & 15;
     const int qd = lane >> 4;
-    u32x4_t qf[KL];
+    u32x4_t qf[NL];
     if (col < G) {
-        const u32x4_t* qsrc = reinterpret_cast<const u32x4_t*>(
-            p.q + (((int64_t)b * p.Hq + hq0 + col) * D + qd * KQ) * EB);
+        const char* qrow = p.q + ((int64_t)b * p.Hq + hq0 + col) * D * EB;
 #pragma unroll
-        for (int c = 0; c < KL; ++c) qf[c] = qsrc[c];
+        for (int c = 0; c < NL; ++c)
+            qf[c] = *reinterpret_cast<const u32x4_t*>(qrow + (c * 4 * E + qd * E) * EB);
     } else {
 #pragma unroll
-        for (int c = 0; c < KL; ++c) qf[c] = u32x4_t{0u, 0u, 0u, 0u};
+        for (int c = 0; c < NL; ++c) qf[c] = u32x4_t{0u, 0u, 0u, 0u};
     }
-    __syncthreads();
+    wave_sync();
 
-    const int64_t head_rows = (int64_t)p.bs;              // rows per (block, head) tile
-    const int64_t blk_rows = (int64_t)p.Hkv * head_rows;  // rows per physical block
+    // One stream of 2 * ngroups items: item i < ngroups is K group i, item ngroups + i is
+    // V group i. Each item is NL 16-byte loads per lane; a ring of DEPTH items keeps
+    // DEPTH * NL * 1 KiB in flight per wave, and V loads are already under way while
+    // the softmax statistics of the partition are formed.
+    const int64_t head_rows = (int64_t)p.bs;
+    const int64_t blk_rows = (int64_t)p.Hkv * head_rows;
     const int bs_mask = p.bs - 1;
-
-    // ---- pass 1: scores
-    float m_run = -INFINITY;
-    const int lane_k_off = col * ROW + qd * KQ * EB;   // this lane's K row quarter
-#pragma unroll 2
-    for (int gi = 0; gi < ngroups; ++gi) {
-        const int tl = gi << 4;
-        const int phys = __builtin_amdgcn_readfirstlane(tbl[tl >> p.bs_shift]);
-        const int64_t row0 = (int64_t)phys * blk_rows + g * head_rows + (tl & bs_mask);
-        const u32x4_t* ksrc = reinterpret_cast<const u32x4_t*>(p.k + row0 * ROW + lane_k_off);
-        u32x4_t kf[KL];
-#pragma unroll
-        for (int c = 0; c < KL; ++c) kf[c] = __builtin_nontemporal_load(ksrc + c);
-        const f32x4_t sc = qk_tile<BF16, KL>(kf, qf);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = tl + 4 * qd + i;
-            const float s = (t < ntok) ? sc[i] * p.scale_log2 : -INFINITY;
-            if (col < G) s_lds[t * G + col] = s;
-            m_run = fmaxf(m_run, s);
-        }
-    }
-    // lanes col, col+16, col+32, col+48 hold the same head
-    m_run = fmaxf(m_run, __shfl_xor(m_run, 16));
-    m_run = fmaxf(m_run, __shfl_xor(m_run, 32));
-    __syncthreads();
-
-    // ---- pass 2: probabilities in place, per-head sums (lane handles head lane % G)
-    const float m_mine = __shfl(m_run, lane % G);
-    float l_sum = 0.f;
-    const int nent = ngroups * 16 * G;
-    for (int e = lane; e < nent; e += 64) {
-        const float pe = __builtin_amdgcn_exp2f(s_lds[e] - m_mine);
-        s_lds[e] = pe;
-        l_sum += pe;
-    }
-#pragma unroll
-    for (int off = G; off < 64; off <<= 1) l_sum += __shfl_xor(l_sum, off);
-    __syncthreads();
-
-    // ---- pass 3: o = sum_t p_t v_t
+    const int lane_k_off = col * ROW + qd * 16;        // K: row `col`, piece `qd` (+64 B per load)
     const int vrow = lane / O;
     const int voct = lane % O;
+    const int lane_v_off = vrow * ROW + voct * 16;     // V: row `vrow` (+R per load), slice voct
+    const int nitems = 2 * ngroups;
+
+    // Loads are issued unconditionally and in program order (past the end the index is
+    // clamped to the last item, a re-read that hits in cache), so the compiler can keep
+    // DEPTH - 1 items outstanding while it consumes one.
+    auto issue = [&](int item, u32x4_t (&dst)[NL]) {
+        item = item < nitems ? item : nitems - 1;
+        const bool is_v = item >= ngroups;
+        const int tl = (is_v ? item - ngroups : item) << 4;
+        const int phys = __builtin_amdgcn_readfirstlane(tbl[tl >> p.bs_shift]);
+        const int64_t row0 = (int64_t)phys * blk_rows + g * head_rows + (tl & bs_mask);
+        const char* sbase = (is_v ? p.v : p.k) + row0 * ROW;
+        const uint32_t voff = is_v ? lane_v_off : lane_k_off;
+        const uint32_t vstride = is_v ? R * ROW : 64;
+#pragma unroll
+        for (int c = 0; c < NL; ++c)
+            dst[c] = load16(reinterpret_cast<const u32x4_t*>(sbase + voff + c * vstride));
+    };
+
+    u32x4_t ring[DEPTH][NL];
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) issue(j, ring[j]);
+
+    float m_run = -INFINITY;
+    float l_sum = 0.f;
     float acc[G][E];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
-    const int lane_v_off = vrow * ROW + voct * 16;
-#pragma unroll 2
-    for (int gi = 0; gi < ngroups; ++gi) {
-        const int tl = gi << 4;
-        const int phys = __builtin_amdgcn_readfirstlane(tbl[tl >> p.bs_shift]);
-        const int64_t row0 = (int64_t)phys * blk_rows + g * head_rows + (tl & bs_mask);
-        const char* vsrc = p.v + row0 * ROW + lane_v_off;
-        u32x4_t vf[VL];
+
+    for (int i0 = 0; i0 < nitems; i0 += DEPTH) {
 #pragma unroll
-        for (int k = 0; k < VL; ++k)
-            vf[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vsrc + k * R * ROW));
-        if (tl + 16 > ntok) {   // last, partly valid group: zero rows past the end
+        for (int j = 0; j < DEPTH; ++j) {
+            const int it = i0 + j;
+            if (it < nitems) {
+                if (it < ngroups) {
+                    // ---- scores of K group `it` on the matrix cores
+                    const int tl = it << 4;
+                    const f32x4_t sc = qk_tile<BF16, NL>(ring[j], qf);
 #pragma unroll
-            for (int k = 0; k < VL; ++k)
-                if (tl + vrow + k * R >= ntok) vf[k] = u32x4_t{0u, 0u, 0u, 0u};
-        }
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = tl + 4 * qd + i;
+                        const float s = (t < ntok) ? sc[i] * p.scale_log2 : -INFINITY;
+                        if (col < G) s_lds[t * G + col] = s;
+                        m_run = fmaxf(m_run, s);
+                    }
+                    if (it == ngroups - 1) {
+                        // ---- partition statistics: per-head max, p = exp2(s - m), sums
+                        m_run = fmaxf(m_run, __shfl_xor(m_run, 16));
+                        m_run = fmaxf(m_run, __shfl_xor(m_run, 32));
+                        wave_sync();
+                        const float m_mine = __shfl(m_run, lane % G);
+                        const int nent = ngroups * 16 * G;
+                        for (int e = lane; e < nent; e += 64) {
+                            const float pe = __builtin_amdgcn_exp2f(s_lds[e] - m_mine);
+                            s_lds[e] = pe;
+                            l_sum += pe;
+                        }
 #pragma unroll
-        for (int k = 0; k < VL; ++k) {
-            float pk[G];
-            load_probs<G>(s_lds + (tl + vrow + k * R) * G, pk);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t u = vf[k][w];
-                if constexpr (BF16) {
-                    const float x0 = lo_bf16(u), x1 = hi_bf16(u);
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        acc[h][2 * w] = fmaf(pk[h], x0, acc[h][2 * w]);
-                        acc[h][2 * w + 1] = fmaf(pk[h], x1, acc[h][2 * w + 1]);
+                        for (int off = G; off < 64; off <<= 1) l_sum += __shfl_xor(l_sum, off);
+                        wave_sync();
                     }
                 } else {
-                    const float x = __uint_as_float(u);
+                    // ---- o += p * V for V group `it - ngroups` on the vector ALUs
+                    const int tl = (it - ngroups) << 4;
+                    if (tl + 16 > ntok) {   // last, partly valid group: zero rows past the end
 #pragma unroll
-                    for (int h = 0; h < G; ++h) acc[h][w] = fmaf(pk[h], x, acc[h][w]);
+                        for (int k = 0; k < NL; ++k)
+                            if (tl + vrow + k * R >= ntok) ring[j][k] = u32x4_t{0u, 0u, 0u, 0u};
+                    }
+#pragma unroll
+                    for (int k = 0; k < NL; ++k) {
+                        float pk[G];
+                        load_probs<G>(s_lds + (tl + vrow + k * R) * G, pk);
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            const uint32_t u = ring[j][k][w];
+                            if constexpr (BF16) {
+                                const float x0 = lo_bf16(u), x1 = hi_bf16(u);
+#pragma unroll
+                                for (int h = 0; h < G; ++h) {
+                                    acc[h][2 * w] = fmaf(pk[h], x0, acc[h][2 * w]);
+                                    acc[h][2 * w + 1] = fmaf(pk[h], x1, acc[h][2 * w + 1]);
+                                }
+                            } else {
+                                const float x = __uint_as_float(u);
+#pragma unroll
+                                for (int h = 0; h < G; ++h) acc[h][w] = fmaf(pk[h], x, acc[h][w]);
+                            }
+                        }
+                    }
                 }
             }
+            issue(it + DEPTH, ring[j]);
         }
     }
+
     // sum the R row-groups that share a column slice
 #pragma unroll
     for (int off = O; off < 64; off <<= 1)
@@ -288,6 +347,331 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
         }
         if (lane < G) {   // lane h holds head h's max (col == h) and sum (h % G == h)
             p.ws_ml[((int64_t)b * p.Hq + hq0 + lane) * p.n_parts + part] = make_float2(m_run, l_sum);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// bf16 caches: one pass per partition, K and V of each 16-token group loaded together,
+// both contractions on the matrix cores.
+//
+// QK^T: v_mfma_f32_16x16x32_bf16 with A = the 16 K rows of the group and B = query heads.
+// MFMA row m = 4r + i carries token r + 4i (r = lane / 16 of the lane feeding that row
+// is not the same r; the permutation only decides which row each lane loads), and the 16
+// columns carry the group's 4 heads of a head set, each repeated 4 times. Then lane
+// (r = lane / 16, c = lane % 16) receives in register i the score of token r + 4i for head
+// c % 4, which is exactly the A operand that v_mfma_f32_4x4x1_16b_f32 (16 blocks of
+// 4 x 4 x 1) needs for PV: block lanes 4b..4b+3 (all of row group r) supply
+// p[head lane % 4][token r + 4i] and, as B, one element of V row r + 4i, the element a
+// coalesced 16-byte load of that row already holds. PV therefore needs no transpose, no
+// LDS and no cross-lane exchange; the four row groups' partial sums are added at the end.
+//
+// Softmax: online, per head: the running maximum is updated every group and the
+// accumulators and running sum are multiplied by exp2(old max - new max), a factor that is
+// exactly 1 when the maximum did not move (branch-free, so the accumulators keep their
+// registers).
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <int W> struct VecOf;
+template <> struct VecOf<16> { typedef u32x4_t type; };
+template <> struct VecOf<8> { typedef u32x2_t type; };
+
+// Sum / max over the four 16-lane row groups without LDS traffic: gfx950's permlane swaps
+// exchange the odd rows (16 lanes) / the upper half (32 lanes) of one register with the
+// even rows / lower half of another. Given two registers holding the same values, they
+// then hold the row pairs (0,1),(2,3) crosswise, so one add or max completes a butterfly
+// step. Both registers are outputs of the instruction, so it is written as inline
+// assembly with two read-write operands (preceded by the wait states a VALU result needs
+// before a permlane reads it).
+__device__ __forceinline__ void swap_rows16(uint32_t& a, uint32_t& b) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_halves(uint32_t& a, uint32_t& b) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+    uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+    swap_rows16(a, b);
+    uint32_t c = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+    uint32_t d = c;
+    swap_halves(c, d);
+    return __builtin_bit_cast(float, c) + __builtin_bit_cast(float, d);
+}
+__device__ __forceinline__ float rows_max(float v) {
+    uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+    swap_rows16(a, b);
+    uint32_t c = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)));
+    uint32_t d = c;
+    swap_halves(c, d);
+    return fmaxf(__builtin_bit_cast(float, c), __builtin_bit_cast(float, d));
+}
+// value of lane (lane & ~3) + m of the same quad, via DPP
+__device__ __forceinline__ float quad_bcast(float v, int m) {
+    const int x = __builtin_bit_cast(int, v);
+    int y;
+    switch (m) {
+        case 0: y = __builtin_amdgcn_mov_dpp(x, 0x00, 0xf, 0xf, false); break;
+        case 1: y = __builtin_amdgcn_mov_dpp(x, 0x55, 0xf, 0xf, false); break;
+        case 2: y = __builtin_amdgcn_mov_dpp(x, 0xaa, 0xf, 0xf, false); break;
+        default: y = __builtin_amdgcn_mov_dpp(x, 0xff, 0xf, 0xf, false); break;
+    }
+    return __builtin_bit_cast(float, y);
+}
+
+template <int D, int G, int DEPTH>
+__global__ __launch_bounds__(64) void decode_bf16_kernel(Params p) {
+    constexpr int ROW = D * 2;              // bytes per cached row
+    constexpr int NK = D / 32;              // 16-byte K loads per lane = QK MFMA steps
+    constexpr int WV = D / 8;               // bytes of a V row per lane per load (16 or 8)
+    constexpr int EV = D / 16;              // bf16 elements per lane per V load
+    constexpr int NSET = (G + 3) / 4;       // head sets of 4
+    constexpr int G4 = G < 4 ? G : 4;       // distinct heads in a set
+    typedef typename VecOf<WV>::type vload_t;
+    static_assert(D == 64 || D == 128, "head size");
+
+    const int lane = threadIdx.x;
+    int g, b, part;
+    work_item(p, g, b, part);
+    const int cap = p.max_blocks * p.bs;
+    int L = p.lens[b];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    const int hq0 = g * G;
+    // Partitions are counted from the end of the sequence in whole 16-token groups:
+    // partition 0 holds the last part_tokens / 16 groups, and the highest-numbered one,
+    // the short remainder at the start of the sequence. Workgroups are dispatched in
+    // partition order, so the last ones to start are the short remainders of the longest
+    // sequences, which keeps the end of the grid from waiting on full partitions.
+    const int seq_groups = (L + 15) >> 4;
+    const int part_groups = p.part_tokens >> 4;
+    const int g_end = seq_groups - part * part_groups;
+    if (g_end <= 0) {
+        if (part == 0) {   // empty sequence: a zero row per head
+            for (int i = lane; i < G * D; i += 64)
+                p.out[((int64_t)b * p.Hq + hq0) * D + i] = 0.f;
+        }
+        return;
+    }
+    const int g_start = g_end > part_groups ? g_end - part_groups : 0;
+    const int t0 = g_start << 4;                                   // first token
+    const int ngroups = g_end - g_start;
+    const int ntok = (part == 0 ? L : (g_end << 4)) - t0;         // valid tokens
+    const int nparts_b = (seq_groups + part_groups - 1) / part_groups;
+
+    const int r = lane >> 4;     // row group
+    const int c = lane & 15;     // column
+    // query fragments, B operand of QK: column c of set s is head 4s + (c % 4) % G4
+    u32x4_t qf[NSET][NK];
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+        const int h = 4 * s + ((c & 3) % G4);
+        const char* qrow = p.q + ((int64_t)b * p.Hq + hq0 + h) * ROW;
+#pragma unroll
+        for (int k = 0; k < NK; ++k)
+            qf[s][k] = *reinterpret_cast<const u32x4_t*>(qrow + (k * 32 + r * 8) * 2);
+    }
+
+    const int blk0 = t0 >> p.bs_shift;
+    const int32_t* trow = p.tables + (int64_t)b * p.max_blocks + blk0;
+    const int64_t tile_bytes = (int64_t)p.bs * ROW;              // one (block, head) tile
+    const int64_t blk_bytes = (int64_t)p.Hkv * tile_bytes;       // one physical block
+    const char* kbase = p.k + g * tile_bytes;
+    const char* vbase = p.v + g * tile_bytes;
+    const int bs_mask = p.bs - 1;
+    const int last = ngroups - 1;
+    // K: lane feeds MFMA row c, i.e. token (c / 4) + 4 (c % 4) of the group, 16 bytes at
+    // 64 k + 16 r; V: row r (+4 per load), bytes c * WV of the row
+    const uint32_t koff = (uint32_t)(((c >> 2) + 4 * (c & 3)) * ROW + r * 16);
+    const uint32_t voff = (uint32_t)(r * ROW + c * WV);
+
+    struct Slot {
+        u32x4_t k[NK];
+        vload_t v[4];
+    };
+    // physical block of group gi (clamped into the sequence and into the pool)
+    // The partition's block-table slice, clamped into the pool, is staged in LDS once;
+    // the loop then reads one entry per group (LDS reads return in order, so waiting for
+    // one does not wait for the global loads in flight).
+    __shared__ int tbl[pa_internal::kMaxPartTokens / 16 + 1];
+    const int nblk = ((t0 + (ngroups << 4) - 1) >> p.bs_shift) - blk0 + 1;
+    for (int i = lane; i < nblk; i += 64) {
+        const int e = trow[i];
+        tbl[i] = e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);
+    }
+    wave_sync();
+    // table entry of group gi (clamped into the sequence)
+    auto entry_of = [&](int gi) {
+        gi = gi < last ? gi : last;
+        return __builtin_amdgcn_readfirstlane(tbl[((t0 + (gi << 4)) >> p.bs_shift) - blk0]);
+    };
+    auto issue = [&](int gi, int ph, Slot& dst) {
+        gi = gi < last ? gi : last;
+        const int64_t off = (int64_t)ph * blk_bytes + (int64_t)((t0 + (gi << 4)) & bs_mask) * ROW;
+        const char* kb = kbase + off;
+        const char* vb = vbase + off;
+#pragma unroll
+        for (int k = 0; k < NK; ++k)
+            dst.k[k] = *reinterpret_cast<const u32x4_t*>(kb + koff + k * 64);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            dst.v[k] = *reinterpret_cast<const vload_t*>(vb + voff + k * 4 * ROW);
+    };
+
+    f32x4_t acc[NSET][EV];
+    float m_ref[NSET], l_run[NSET];
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+        m_ref[s] = -INFINITY;
+        l_run[s] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) acc[s][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const float cl2 = p.scale_log2;
+
+    // one 16-token group: scores on MFMA, online softmax, PV on MFMA
+    auto consume = [&](Slot& sl, int gi, bool masked) {
+        const int tl = gi << 4;
+        float pr[NSET][4];
+#pragma unroll
+        for (int s = 0; s < NSET; ++s) {
+            f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < NK; ++k)
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, sl.k[k]), __builtin_bit_cast(bf16x8_t, qf[s][k]),
+                    sc, 0, 0, 0);
+            // scores in log2 units; the largest one then gets exactly p = 1
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = sc[i] * cl2;
+            if (masked) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = (tl + r + 4 * i < ntok) ? x[i] : -INFINITY;
+            }
+            // running maximum and the factor that moves earlier terms onto it (exactly 1
+            // when the maximum did not change, 0 on the first group)
+            const float cand = rows_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+            const float m_new = fmaxf(m_ref[s], cand);
+            const float alpha = __builtin_amdgcn_exp2f(m_ref[s] - m_new);
+            l_run[s] *= alpha;
+            m_ref[s] = m_new;
+            // accumulator register m holds head m, whose factor sits in quad lane m
+            float am[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) am[m] = quad_bcast(alpha, m);
+#pragma unroll
+            for (int e = 0; e < EV; ++e)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) acc[s][e][m] *= am[m];
+            const float mr = m_new;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e2 = __builtin_amdgcn_exp2f(x[i] - mr);
+                pr[s][i] = masked ? ((x[i] == -INFINITY) ? 0.f : e2) : e2;
+            }
+            l_run[s] += (pr[s][0] + pr[s][1]) + (pr[s][2] + pr[s][3]);
+        }
+        if (masked) {   // V rows past the end may hold anything: zero them
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (tl + r + 4 * k >= ntok) sl.v[k] = vload_t{};
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+#pragma unroll
+            for (int w = 0; w < WV / 4; ++w) {
+                const uint32_t u = sl.v[k][w];
+                const float v0 = lo_bf16(u), v1 = hi_bf16(u);
+#pragma unroll
+                for (int s = 0; s < NSET; ++s) {
+                    acc[s][2 * w] = __builtin_amdgcn_mfma_f32_4x4x1f32(pr[s][k], v0, acc[s][2 * w], 0, 0, 0);
+                    acc[s][2 * w + 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(pr[s][k], v1, acc[s][2 * w + 1], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // Ring of DEPTH groups: group gi lives in slot gi % DEPTH. The main loop runs over
+    // whole chunks of DEPTH groups, all of them full (the last group, which may be partly
+    // valid, is always left to the masked remainder), and its body is straight-line:
+    // consume slot j, then refill it with the group DEPTH ahead (clamped past the end).
+    // Scheduling barriers keep the compiler from sinking the refill loads to their use,
+    // so DEPTH - 1 groups stay in flight while one is consumed. Block numbers for a
+    // chunk's refills are read one chunk ahead.
+    Slot ring[DEPTH];
+    int ph_next[DEPTH];
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) issue(j, entry_of(j), ring[j]);
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) ph_next[j] = entry_of(j + DEPTH);
+
+    const int n_main = (last / DEPTH) * DEPTH;   // groups handled by the main loop
+    for (int g0 = 0; g0 < n_main; g0 += DEPTH) {
+        int ph_cur[DEPTH];
+#pragma unroll
+        for (int j = 0; j < DEPTH; ++j) {
+            ph_cur[j] = ph_next[j];
+            ph_next[j] = entry_of(g0 + j + 2 * DEPTH);
+        }
+#pragma unroll
+        for (int j = 0; j < DEPTH; ++j) {
+            consume(ring[j], g0 + j, false);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(g0 + j + DEPTH, ph_cur[j], ring[j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // remainder: groups n_main .. last (1 to DEPTH of them), masked
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+        if (n_main + j <= last) consume(ring[j], n_main + j, true);
+    }
+
+    // add the four row groups' partial sums (lanes c, c + 16, c + 32, c + 48)
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+        l_run[s] = rows_sum(l_run[s]);
+#pragma unroll
+        for (int e = 0; e < EV; ++e)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc[s][e][m] = rows_sum(acc[s][e][m]);
+    }
+    // lane c (row group 0) now holds, for head m of each set, output columns
+    // c*EV .. c*EV+EV-1; head m's sum and reference maximum sit in quad lane m
+    float lh[NSET][4], mh[NSET][4];
+#pragma unroll
+    for (int s = 0; s < NSET; ++s)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            lh[s][m] = quad_bcast(l_run[s], m);
+            mh[s][m] = quad_bcast(m_ref[s], m);
+        }
+    if (r == 0) {
+#pragma unroll
+        for (int s = 0; s < NSET; ++s) {
+#pragma unroll
+            for (int m = 0; m < G4; ++m) {
+                const int h = 4 * s + m;
+                float o[EV];
+#pragma unroll
+                for (int e = 0; e < EV; ++e) o[e] = acc[s][e][m];
+                if (nparts_b == 1) {
+                    const float inv = 1.0f / lh[s][m];
+                    float* dst = p.out + ((int64_t)b * p.Hq + hq0 + h) * D + c * EV;
+#pragma unroll
+                    for (int e = 0; e < EV; e += 4)
+                        *reinterpret_cast<float4*>(dst + e) =
+                            make_float4(o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv);
+                } else {
+                    float* dst = p.ws_o + (((int64_t)b * p.Hq + hq0 + h) * p.n_parts + part) * D + c * EV;
+#pragma unroll
+                    for (int e = 0; e < EV; e += 4)
+                        *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+                    if (c == 0)
+                        p.ws_ml[((int64_t)b * p.Hq + hq0 + h) * p.n_parts + part] =
+                            make_float2(mh[s][m], lh[s][m]);
+                }
+            }
         }
     }
 }
@@ -353,13 +737,26 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
     }
 }
 
+#ifndef PA_DECODE_DEPTH
+#define PA_DECODE_DEPTH 4
+#endif
+
+#ifndef PA_BF16_DEPTH
+#define PA_BF16_DEPTH 2
+#endif
+
 template <bool BF16, int D, int G>
 hipError_t launch_one(const Params& prm, int B, int Hkv, void* stream) {
-    const size_t lds = (size_t)prm.part_tokens * G * sizeof(float) +
-                       (size_t)(prm.part_tokens / 16) * sizeof(int);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G>), dim3(prm.n_parts, Hkv, B), dim3(64),
-                       lds, s, prm);
+    if constexpr (BF16) {
+        hipLaunchKernelGGL((decode_bf16_kernel<D, G, PA_BF16_DEPTH>), dim3(prm.n_parts * Hkv * B),
+                           dim3(64), 0, s, prm);
+    } else {
+        const size_t lds = (size_t)prm.part_tokens * G * sizeof(float) +
+                           (size_t)(prm.part_tokens / 16) * sizeof(int);
+        hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G, PA_DECODE_DEPTH>),
+                           dim3(prm.n_parts * Hkv * B), dim3(64), lds, s, prm);
+    }
     if (prm.n_parts > 1)
         hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(prm.Hq, B), dim3(256), 0, s, prm);
     return hipGetLastError();
@@ -397,6 +794,7 @@ int launch_decode(const DecodeLaunch& a, const char** err) {
     prm.v = static_cast<const char*>(a.v);
     prm.tables = a.tables;
     prm.lens = a.lens;
+    prm.B = a.B;
     prm.Hq = a.Hq;
     prm.Hkv = a.Hkv;
     prm.bs = a.bs;
