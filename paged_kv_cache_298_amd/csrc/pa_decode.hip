@@ -33,6 +33,22 @@
 
 #include "pa_internal.h"
 
+// Build-time tuning knobs: ring depth (16-token groups in flight per wave) of the bf16 and
+// fp32 kernels, and whether the bf16 kernel computes a ring's groups back to back before
+// refilling them.
+#ifndef PA_BF16_DEPTH
+#define PA_BF16_DEPTH 4
+#endif
+#ifndef PA_BF16_CHUNK
+#define PA_BF16_CHUNK 8
+#endif
+#ifndef PA_BF16_QLDS
+#define PA_BF16_QLDS 0
+#endif
+#ifndef PA_DECODE_DEPTH
+#define PA_DECODE_DEPTH 4
+#endif
+
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -366,10 +382,12 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
 // coalesced 16-byte load of that row already holds. PV therefore needs no transpose, no
 // LDS and no cross-lane exchange; the four row groups' partial sums are added at the end.
 //
-// Softmax: online, per head: the running maximum is updated every group and the
-// accumulators and running sum are multiplied by exp2(old max - new max), a factor that is
-// exactly 1 when the maximum did not move (branch-free, so the accumulators keep their
-// registers).
+// Work is done in chunks of kChunk groups (128 tokens): the chunk's kChunk QK^T MFMA
+// chains are independent, then one online-softmax update per head (new running maximum,
+// accumulators and running sum multiplied by exp2(old max - new max), a factor that is
+// exactly 1 when the maximum did not move), then the chunk's PV MFMAs. The loads form one
+// stream in consumption order, K of the chunk's groups then V of the same groups, held in
+// a ring of DEPTH items of equal size, so DEPTH - 1 items are in flight while one is used.
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -419,16 +437,18 @@ __device__ __forceinline__ float quad_bcast(float v, int m) {
     return __builtin_bit_cast(float, y);
 }
 
-template <int D, int G, int DEPTH>
+template <int D, int G, int DEPTH, int kChunk, bool QLDS>
 __global__ __launch_bounds__(64) void decode_bf16_kernel(Params p) {
     constexpr int ROW = D * 2;              // bytes per cached row
-    constexpr int NK = D / 32;              // 16-byte K loads per lane = QK MFMA steps
+    constexpr int NQ = D / 32;              // 16-byte registers per ring item
     constexpr int WV = D / 8;               // bytes of a V row per lane per load (16 or 8)
     constexpr int EV = D / 16;              // bf16 elements per lane per V load
     constexpr int NSET = (G + 3) / 4;       // head sets of 4
     constexpr int G4 = G < 4 ? G : 4;       // distinct heads in a set
+    constexpr int ITEMS = 2 * kChunk;       // ring items per chunk: K groups, then V groups
     typedef typename VecOf<WV>::type vload_t;
     static_assert(D == 64 || D == 128, "head size");
+    static_assert(kChunk % DEPTH == 0, "the ring depth must divide the chunk");
 
     const int lane = threadIdx.x;
     int g, b, part;
@@ -437,195 +457,224 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(Params p) {
     int L = p.lens[b];
     L = L < 0 ? 0 : (L > cap ? cap : L);
     const int hq0 = g * G;
-    // Partitions are counted from the end of the sequence in whole 16-token groups:
-    // partition 0 holds the last part_tokens / 16 groups, and the highest-numbered one,
-    // the short remainder at the start of the sequence. Workgroups are dispatched in
-    // partition order, so the last ones to start are the short remainders of the longest
-    // sequences, which keeps the end of the grid from waiting on full partitions.
-    const int seq_groups = (L + 15) >> 4;
-    const int part_groups = p.part_tokens >> 4;
-    const int g_end = seq_groups - part * part_groups;
-    if (g_end <= 0) {
+    const int t0 = part * p.part_tokens;
+    // The block-table slice of the partition is fetched before the sequence length is
+    // known (it does not depend on it): lane i holds entry i, clamped into the row and
+    // into the pool, and the loop reads it with v_readlane.
+    const int blk0 = t0 >> p.bs_shift;
+    int tblv;
+    {
+        const int32_t* trow = p.tables + (int64_t)b * p.max_blocks;
+        int i = blk0 + lane;
+        i = i < p.max_blocks ? i : p.max_blocks - 1;
+        const int e = trow[i];
+        tblv = e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);
+    }
+    if (t0 >= L) {
         if (part == 0) {   // empty sequence: a zero row per head
             for (int i = lane; i < G * D; i += 64)
                 p.out[((int64_t)b * p.Hq + hq0) * D + i] = 0.f;
         }
         return;
     }
-    const int g_start = g_end > part_groups ? g_end - part_groups : 0;
-    const int t0 = g_start << 4;                                   // first token
-    const int ngroups = g_end - g_start;
-    const int ntok = (part == 0 ? L : (g_end << 4)) - t0;         // valid tokens
-    const int nparts_b = (seq_groups + part_groups - 1) / part_groups;
+    const int ntok = min(p.part_tokens, L - t0);
+    const int ngroups = (ntok + 15) >> 4;
+    const int last = ngroups - 1;
+    const int nchunks = (ngroups + kChunk - 1) / kChunk;
+    const int nparts_b = (L + p.part_tokens - 1) / p.part_tokens;
 
     const int r = lane >> 4;     // row group
     const int c = lane & 15;     // column
-    // query fragments, B operand of QK: column c of set s is head 4s + (c % 4) % G4
-    u32x4_t qf[NSET][NK];
+    // query fragments, B operand of QK: column c of set s is head 4s + (c % 4) % G4; held
+    // in registers, or (QLDS) parked in LDS and re-read per group to save registers
+    u32x4_t qf[QLDS ? 1 : NSET][QLDS ? 1 : NQ];
+    __shared__ u32x4_t q_lds[QLDS ? NSET * NQ * 64 : 1];
 #pragma unroll
     for (int s = 0; s < NSET; ++s) {
         const int h = 4 * s + ((c & 3) % G4);
         const char* qrow = p.q + ((int64_t)b * p.Hq + hq0 + h) * ROW;
 #pragma unroll
-        for (int k = 0; k < NK; ++k)
-            qf[s][k] = *reinterpret_cast<const u32x4_t*>(qrow + (k * 32 + r * 8) * 2);
+        for (int k = 0; k < NQ; ++k) {
+            const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + (k * 32 + r * 8) * 2);
+            if constexpr (QLDS) q_lds[(s * NQ + k) * 64 + lane] = x;
+            else qf[s][k] = x;
+        }
     }
+    auto qfrag = [&](int s, int k) -> u32x4_t {
+        if constexpr (QLDS) return q_lds[(s * NQ + k) * 64 + lane];
+        else return qf[s][k];
+    };
+    if constexpr (QLDS) wave_sync();
 
-    const int blk0 = t0 >> p.bs_shift;
-    const int32_t* trow = p.tables + (int64_t)b * p.max_blocks + blk0;
     const int64_t tile_bytes = (int64_t)p.bs * ROW;              // one (block, head) tile
     const int64_t blk_bytes = (int64_t)p.Hkv * tile_bytes;       // one physical block
     const char* kbase = p.k + g * tile_bytes;
     const char* vbase = p.v + g * tile_bytes;
     const int bs_mask = p.bs - 1;
-    const int last = ngroups - 1;
     // K: lane feeds MFMA row c, i.e. token (c / 4) + 4 (c % 4) of the group, 16 bytes at
     // 64 k + 16 r; V: row r (+4 per load), bytes c * WV of the row
     const uint32_t koff = (uint32_t)(((c >> 2) + 4 * (c & 3)) * ROW + r * 16);
     const uint32_t voff = (uint32_t)(r * ROW + c * WV);
 
-    struct Slot {
-        u32x4_t k[NK];
-        vload_t v[4];
+    struct Item {
+        u32x4_t q[NQ];
     };
-    // physical block of group gi (clamped into the sequence and into the pool)
-    // The partition's block-table slice, clamped into the pool, is staged in LDS once;
-    // the loop then reads one entry per group (LDS reads return in order, so waiting for
-    // one does not wait for the global loads in flight).
-    __shared__ int tbl[pa_internal::kMaxPartTokens / 16 + 1];
-    const int nblk = ((t0 + (ngroups << 4) - 1) >> p.bs_shift) - blk0 + 1;
-    for (int i = lane; i < nblk; i += 64) {
-        const int e = trow[i];
-        tbl[i] = e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);
-    }
-    wave_sync();
-    // table entry of group gi (clamped into the sequence)
-    auto entry_of = [&](int gi) {
+    // load stream item t of chunk ch (t < kChunk: K of group t, else V of group t - kChunk);
+    // groups past the partition are clamped to its last group (a re-read that hits in cache)
+    auto issue = [&](int ch, int t, Item& dst) {
+        const bool is_v = t >= kChunk;
+        int gi = ch * kChunk + (is_v ? t - kChunk : t);
         gi = gi < last ? gi : last;
-        return __builtin_amdgcn_readfirstlane(tbl[((t0 + (gi << 4)) >> p.bs_shift) - blk0]);
+        const int ph = __builtin_amdgcn_readlane(tblv, (gi << 4) >> p.bs_shift);
+        const int64_t off = (int64_t)ph * blk_bytes + (int64_t)((gi << 4) & bs_mask) * ROW;
+        if (!is_v) {
+            const char* kb = kbase + off;
+#pragma unroll
+            for (int k = 0; k < NQ; ++k)
+                dst.q[k] = *reinterpret_cast<const u32x4_t*>(kb + koff + k * 64);
+        } else {
+            const char* vb = vbase + off;
+            if constexpr (WV == 16) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    dst.q[k] = *reinterpret_cast<const u32x4_t*>(vb + voff + k * 4 * ROW);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; k += 2) {
+                    const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vb + voff + k * 4 * ROW);
+                    const u32x2_t e = *reinterpret_cast<const u32x2_t*>(vb + voff + (k + 1) * 4 * ROW);
+                    dst.q[k / 2] = __builtin_shufflevector(a, e, 0, 1, 2, 3);
+                }
+            }
+        }
     };
-    auto issue = [&](int gi, int ph, Slot& dst) {
-        gi = gi < last ? gi : last;
-        const int64_t off = (int64_t)ph * blk_bytes + (int64_t)((t0 + (gi << 4)) & bs_mask) * ROW;
-        const char* kb = kbase + off;
-        const char* vb = vbase + off;
-#pragma unroll
-        for (int k = 0; k < NK; ++k)
-            dst.k[k] = *reinterpret_cast<const u32x4_t*>(kb + koff + k * 64);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            dst.v[k] = *reinterpret_cast<const vload_t*>(vb + voff + k * 4 * ROW);
+    // dword w of V load k within an item
+    auto vword = [&](const Item& it, int k, int w) -> uint32_t {
+        if constexpr (WV == 16) return it.q[k][w];
+        else return it.q[k >> 1][(k & 1) * 2 + w];
     };
 
     f32x4_t acc[NSET][EV];
-    float m_ref[NSET], l_run[NSET];
+    float m_run[NSET], l_run[NSET];
 #pragma unroll
     for (int s = 0; s < NSET; ++s) {
-        m_ref[s] = -INFINITY;
+        m_run[s] = -INFINITY;
         l_run[s] = 0.f;
 #pragma unroll
         for (int e = 0; e < EV; ++e) acc[s][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     const float cl2 = p.scale_log2;
 
-    // one 16-token group: scores on MFMA, online softmax, PV on MFMA
-    auto consume = [&](Slot& sl, int gi, bool masked) {
-        const int tl = gi << 4;
-        float pr[NSET][4];
+    Item ring[DEPTH];
 #pragma unroll
-        for (int s = 0; s < NSET; ++s) {
-            f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < DEPTH; ++j) issue(0, j, ring[j]);
+
+    // One chunk: consume its 2 * kChunk stream items in order, refilling each ring slot
+    // with the item DEPTH positions later. `masked` (the last chunk only) handles tokens
+    // past the end of the partition and groups past its last one.
+    auto chunk = [&](int ch, bool masked) {
+        float y[NSET][kChunk][4];   // scores in log2 units, then probabilities
 #pragma unroll
-            for (int k = 0; k < NK; ++k)
-                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, sl.k[k]), __builtin_bit_cast(bf16x8_t, qf[s][k]),
-                    sc, 0, 0, 0);
-            // scores in log2 units; the largest one then gets exactly p = 1
-            float x[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = sc[i] * cl2;
-            if (masked) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = (tl + r + 4 * i < ntok) ? x[i] : -INFINITY;
-            }
-            // running maximum and the factor that moves earlier terms onto it (exactly 1
-            // when the maximum did not change, 0 on the first group)
-            const float cand = rows_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-            const float m_new = fmaxf(m_ref[s], cand);
-            const float alpha = __builtin_amdgcn_exp2f(m_ref[s] - m_new);
-            l_run[s] *= alpha;
-            m_ref[s] = m_new;
-            // accumulator register m holds head m, whose factor sits in quad lane m
-            float am[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) am[m] = quad_bcast(alpha, m);
-#pragma unroll
-            for (int e = 0; e < EV; ++e)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) acc[s][e][m] *= am[m];
-            const float mr = m_new;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float e2 = __builtin_amdgcn_exp2f(x[i] - mr);
-                pr[s][i] = masked ? ((x[i] == -INFINITY) ? 0.f : e2) : e2;
-            }
-            l_run[s] += (pr[s][0] + pr[s][1]) + (pr[s][2] + pr[s][3]);
-        }
-        if (masked) {   // V rows past the end may hold anything: zero them
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (tl + r + 4 * k >= ntok) sl.v[k] = vload_t{};
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-#pragma unroll
-            for (int w = 0; w < WV / 4; ++w) {
-                const uint32_t u = sl.v[k][w];
-                const float v0 = lo_bf16(u), v1 = hi_bf16(u);
+        for (int t = 0; t < ITEMS; ++t) {
+            Item& it = ring[t % DEPTH];
+            if (t < kChunk) {
+                // ---- scores of group t on the matrix cores
 #pragma unroll
                 for (int s = 0; s < NSET; ++s) {
-                    acc[s][2 * w] = __builtin_amdgcn_mfma_f32_4x4x1f32(pr[s][k], v0, acc[s][2 * w], 0, 0, 0);
-                    acc[s][2 * w + 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(pr[s][k], v1, acc[s][2 * w + 1], 0, 0, 0);
+                    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int k = 0; k < NQ; ++k)
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, it.q[k]),
+                            __builtin_bit_cast(bf16x8_t, qfrag(s, k)), sc, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y[s][t][i] = sc[i] * cl2;
+                }
+                if (t == kChunk - 1) {
+                    // ---- one online-softmax update for the chunk's 128 tokens
+                    const int tc = ch * kChunk * 16;   // first token of the chunk
+#pragma unroll
+                    for (int s = 0; s < NSET; ++s) {
+                        if (masked) {
+#pragma unroll
+                            for (int u = 0; u < kChunk; ++u)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    y[s][u][i] = (tc + u * 16 + r + 4 * i < ntok) ? y[s][u][i] : -INFINITY;
+                        }
+                        float mx = y[s][0][0];
+#pragma unroll
+                        for (int u = 0; u < kChunk; ++u)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, y[s][u][i]);
+                        const float m_new = fmaxf(m_run[s], rows_max(mx));
+                        const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_new);
+                        m_run[s] = m_new;
+                        float am[4];
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) am[m] = quad_bcast(alpha, m);
+#pragma unroll
+                        for (int e = 0; e < EV; ++e)
+#pragma unroll
+                            for (int m = 0; m < 4; ++m) acc[s][e][m] *= am[m];
+                        float ls = 0.f;
+#pragma unroll
+                        for (int u = 0; u < kChunk; ++u) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float e2 = __builtin_amdgcn_exp2f(y[s][u][i] - m_new);
+                                y[s][u][i] = masked ? ((y[s][u][i] == -INFINITY) ? 0.f : e2) : e2;
+                            }
+                            ls += (y[s][u][0] + y[s][u][1]) + (y[s][u][2] + y[s][u][3]);
+                        }
+                        l_run[s] = l_run[s] * alpha + ls;
+                    }
+                }
+            } else {
+                // ---- o += p * V for group u on the matrix cores
+                const int u = t - kChunk;
+                const int gi = ch * kChunk + u;
+                bool skip = false;
+                if (masked) {
+                    skip = gi > last;
+                    if (!skip && gi == last) {   // rows past the end may hold anything
+                        const int tl = gi * 16;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            if (tl + r + 4 * k >= ntok) {
+                                if constexpr (WV == 16) {
+                                    it.q[k] = u32x4_t{0u, 0u, 0u, 0u};
+                                } else {
+                                    it.q[k >> 1][(k & 1) * 2] = 0u;
+                                    it.q[k >> 1][(k & 1) * 2 + 1] = 0u;
+                                }
+                            }
+                        }
+                    }
+                }
+                if (!skip) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+                        for (int w = 0; w < WV / 4; ++w) {
+                            const uint32_t uw = vword(it, k, w);
+                            const float v0 = lo_bf16(uw), v1 = hi_bf16(uw);
+#pragma unroll
+                            for (int s = 0; s < NSET; ++s) {
+                                acc[s][2 * w] = __builtin_amdgcn_mfma_f32_4x4x1f32(y[s][u][k], v0, acc[s][2 * w], 0, 0, 0);
+                                acc[s][2 * w + 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(y[s][u][k], v1, acc[s][2 * w + 1], 0, 0, 0);
+                            }
+                        }
+                    }
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            issue(ch + (t + DEPTH) / ITEMS, (t + DEPTH) % ITEMS, it);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
-
-    // Ring of DEPTH groups: group gi lives in slot gi % DEPTH. The main loop runs over
-    // whole chunks of DEPTH groups, all of them full (the last group, which may be partly
-    // valid, is always left to the masked remainder), and its body is straight-line:
-    // consume slot j, then refill it with the group DEPTH ahead (clamped past the end).
-    // Scheduling barriers keep the compiler from sinking the refill loads to their use,
-    // so DEPTH - 1 groups stay in flight while one is consumed. Block numbers for a
-    // chunk's refills are read one chunk ahead.
-    Slot ring[DEPTH];
-    int ph_next[DEPTH];
-#pragma unroll
-    for (int j = 0; j < DEPTH; ++j) issue(j, entry_of(j), ring[j]);
-#pragma unroll
-    for (int j = 0; j < DEPTH; ++j) ph_next[j] = entry_of(j + DEPTH);
-
-    const int n_main = (last / DEPTH) * DEPTH;   // groups handled by the main loop
-    for (int g0 = 0; g0 < n_main; g0 += DEPTH) {
-        int ph_cur[DEPTH];
-#pragma unroll
-        for (int j = 0; j < DEPTH; ++j) {
-            ph_cur[j] = ph_next[j];
-            ph_next[j] = entry_of(g0 + j + 2 * DEPTH);
-        }
-#pragma unroll
-        for (int j = 0; j < DEPTH; ++j) {
-            consume(ring[j], g0 + j, false);
-            __builtin_amdgcn_sched_barrier(0);
-            issue(g0 + j + DEPTH, ph_cur[j], ring[j]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    // remainder: groups n_main .. last (1 to DEPTH of them), masked
-#pragma unroll
-    for (int j = 0; j < DEPTH; ++j) {
-        if (n_main + j <= last) consume(ring[j], n_main + j, true);
-    }
+    for (int ch = 0; ch < nchunks - 1; ++ch) chunk(ch, false);
+    chunk(nchunks - 1, true);
 
     // add the four row groups' partial sums (lanes c, c + 16, c + 32, c + 48)
 #pragma unroll
@@ -637,14 +686,14 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(Params p) {
             for (int m = 0; m < 4; ++m) acc[s][e][m] = rows_sum(acc[s][e][m]);
     }
     // lane c (row group 0) now holds, for head m of each set, output columns
-    // c*EV .. c*EV+EV-1; head m's sum and reference maximum sit in quad lane m
+    // c*EV .. c*EV+EV-1; head m's sum and running maximum sit in quad lane m
     float lh[NSET][4], mh[NSET][4];
 #pragma unroll
     for (int s = 0; s < NSET; ++s)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             lh[s][m] = quad_bcast(l_run[s], m);
-            mh[s][m] = quad_bcast(m_ref[s], m);
+            mh[s][m] = quad_bcast(m_run[s], m);
         }
     if (r == 0) {
 #pragma unroll
@@ -737,19 +786,13 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
     }
 }
 
-#ifndef PA_DECODE_DEPTH
-#define PA_DECODE_DEPTH 4
-#endif
 
-#ifndef PA_BF16_DEPTH
-#define PA_BF16_DEPTH 2
-#endif
 
 template <bool BF16, int D, int G>
 hipError_t launch_one(const Params& prm, int B, int Hkv, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if constexpr (BF16) {
-        hipLaunchKernelGGL((decode_bf16_kernel<D, G, PA_BF16_DEPTH>), dim3(prm.n_parts * Hkv * B),
+        hipLaunchKernelGGL((decode_bf16_kernel<D, G, PA_BF16_DEPTH, PA_BF16_CHUNK, (PA_BF16_QLDS != 0)>), dim3(prm.n_parts * Hkv * B),
                            dim3(64), 0, s, prm);
     } else {
         const size_t lds = (size_t)prm.part_tokens * G * sizeof(float) +
