@@ -114,7 +114,8 @@ def main():
     _log(f"{wl.name}: B={wl.B} kv_bytes={kv_bytes} pool={wl.num_blocks} blocks, replicas={R}")
 
     reps = []
-    ws_bytes = pa.pa_decode_workspace_bytes(wl.B, wl.Hq, wl.D, wl.block_size, wl.max_blocks)
+    ws_bytes = pa.pa_decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.block_size, wl.max_blocks,
+                                            pa.PA_BF16 if wl.dtype == "bf16" else pa.PA_F32)
     for _ in range(R):
         reps.append(dict(
             q=_to_dev(wl.q, torch, dev), k=_to_dev(wl.k_cache, torch, dev),
@@ -169,18 +170,16 @@ def main():
          f"p50 {np.median(dec_us):.1f}, p90 {np.percentile(dec_us, 90):.1f}")
 
     # ---- hot (one replica, Infinity Cache may help) for context
-    hot = []
     for i in range(args.warmup):
         decode_only(reps[0])
     torch.cuda.synchronize()
-    for i in range(min(args.steps, 50)):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record(stream)
+    n_hot = min(args.steps, 50)
+    for i in range(n_hot):
+        starts[i].record(stream)
         decode_only(reps[0])
-        e.record(stream)
-        hot.append((s, e))
+        ends[i].record(stream)
     torch.cuda.synchronize()
-    hot_us = float(np.mean([s.elapsed_time(e) * 1e3 for s, e in hot]))
+    hot_us = float(np.mean([starts[i].elapsed_time(ends[i]) * 1e3 for i in range(n_hot)]))
 
     achieved = kv_bytes / (dec_mean * 1e-6) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9

@@ -33,11 +33,16 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 /* element types */
 #define PA_F32 0
 #define PA_BF16 1
+
+/* decode work decompositions (pa_set_decode_path) */
+#define PA_PATH_AUTO 0
+#define PA_PATH_PARTITION 1
+#define PA_PATH_STREAM 2
 
 /* status codes */
 #define PA_OK 0
@@ -69,11 +74,19 @@ extern "C" {
  *   seq_lens      device int32 [B]; 0 <= L_b <= max_blocks * block_size
  *   scale         softmax scale, applied in fp32 to the fp32 dot product
  *   workspace     device scratch of at least pa_decode_workspace_bytes(...) bytes, 256-byte
- *                 aligned (may be NULL when that size is 0); it holds split-sequence
- *                 partial results and needs no initialisation
- * Supported: D in {64, 128}; block_size in {16, 32, 64}; G in {1, 2, 4, 8, 16}; others
- * return PA_ERR_UNSUPPORTED. The result is deterministic: repeated calls give identical
- * bits, whatever the physical placement of the blocks.
+ *                 aligned (may be NULL when that size is 0); it holds partial softmax
+ *                 states of sequences split across work items and needs no initialisation
+ * Supported: D in {64, 128}; block_size in {16, 32, 64}; G in {1, 2, 4, 8}; others return
+ * PA_ERR_UNSUPPORTED. The result is deterministic: repeated calls on one device give
+ * identical bits, whatever the physical placement of the blocks.
+ *
+ * Work decomposition (chosen per call, see pa_set_decode_path):
+ *   stream     (bf16 caches, B <= 4096, fewer than 2^31 groups of 16 tokens in the batch):
+ *              the batch's (sequence, KV head) rows, cut into 16-token groups, are laid
+ *              end to end and every resident wavefront of the device takes an equal
+ *              contiguous slice; rows that cross slices are merged by a second kernel.
+ *   partition  (otherwise): one work item per (sequence, KV head, partition of
+ *              pa_decode_partition_tokens tokens), then a merge of the partitions.
  */
 int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* block_tables, const int32_t* seq_lens, int32_t B, int32_t Hq,
@@ -82,11 +95,12 @@ int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_
                   size_t workspace_bytes, void* stream);
 
 /*
- * Workspace bytes pa_decode needs for these sizes (0 when no sequence can span more than
- * one partition). An upper bound taken from the host-known max_blocks.
+ * Workspace bytes pa_decode needs for these sizes and element type, whichever
+ * decomposition it picks (0 when none needs any): an upper bound taken from the
+ * host-known max_blocks. Returns 0 for sizes pa_decode would reject.
  */
-size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t block_size,
-                                 int32_t max_blocks);
+size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                                 int32_t max_blocks, int32_t kv_dtype);
 
 /*
  * Tokens per partition that pa_decode uses for these sizes (a sequence longer than this
@@ -96,10 +110,26 @@ int32_t pa_decode_partition_tokens(int32_t block_size, int32_t max_blocks);
 
 /*
  * Process-wide override of the partition length, for tuning sweeps and tests: tokens must
- * be 0 (automatic) or a multiple of 64 in [64, 8192]. Not thread-safe; affects calls made
+ * be 0 (automatic) or a multiple of 64 in [64, 1024]. Not thread-safe; affects calls made
  * after it returns, including pa_decode_workspace_bytes.
  */
 int32_t pa_set_partition_tokens(int32_t tokens);
+
+/*
+ * Process-wide choice of decomposition, for tests and sweeps: PA_PATH_AUTO (default:
+ * stream where it applies, else partition), PA_PATH_PARTITION, or PA_PATH_STREAM (then
+ * pa_decode returns PA_ERR_UNSUPPORTED where the stream decomposition does not apply).
+ * Not thread-safe.
+ */
+int32_t pa_set_decode_path(int32_t path);
+
+/*
+ * Process-wide stream decomposition settings, for tests and sweeps: waves in [0, 4096]
+ * (0 = every wavefront the device holds at once, else that many, rounded up to a
+ * multiple of 4) and min_slice in [0, 2^20] (0 = default 8): fewer waves are used when
+ * slices would hold fewer than min_slice groups of 16 tokens. Not thread-safe.
+ */
+int32_t pa_set_stream_waves(int32_t waves, int32_t min_slice);
 
 /* ------------------------------------------------------------------ cache write */
 

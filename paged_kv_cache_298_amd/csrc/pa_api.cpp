@@ -14,6 +14,9 @@ namespace {
 
 thread_local std::string g_last_error;
 int32_t g_partition_override = 0;   // 0 = automatic
+int32_t g_path = PA_PATH_AUTO;
+int32_t g_stream_waves = 0;         // 0 = every wave the device holds at once
+int32_t g_min_slice = pa_internal::kDefaultMinSlice;
 
 int32_t fail(int32_t status, const char* fmt, ...) {
     char buf[512];
@@ -65,6 +68,36 @@ size_t workspace_layout(int32_t B, int32_t Hq, int32_t D, int32_t n_parts, size_
     return off + rows * 2 * sizeof(float);
 }
 
+// The stream decomposition serves bf16 caches while the per-sequence prefix fits its LDS
+// and the group count of the whole batch fits 31 bits.
+bool stream_eligible(int32_t kv_dtype, int32_t B, int32_t Hkv, int32_t block_size, int32_t max_blocks) {
+    if (kv_dtype != PA_BF16 || B > pa_internal::kMaxStreamB) return false;
+    const int64_t groups = ((int64_t)block_size * max_blocks + 15) / 16;
+    return (int64_t)B * Hkv * groups < ((int64_t)1 << 31);
+}
+
+struct StreamWs {
+    size_t ml, desc, meta, total;
+};
+
+StreamWs stream_workspace(int32_t G, int32_t D) {
+    const size_t W2 = 2 * (size_t)pa_internal::kMaxStreamWaves;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    StreamWs w;
+    w.ml = up(W2 * (size_t)G * (size_t)D * sizeof(float));
+    w.desc = up(w.ml + W2 * (size_t)G * 2 * sizeof(float));
+    w.meta = up(w.desc + (size_t)pa_internal::kMaxStreamWaves * 4 * sizeof(int32_t));
+    w.total = w.meta + 4 * sizeof(int32_t);
+    return w;
+}
+
+int32_t choose_path(int32_t kv_dtype, int32_t B, int32_t Hkv, int32_t block_size, int32_t max_blocks) {
+    if (g_path == PA_PATH_PARTITION) return pa_internal::kPathPartition;
+    const bool ok = stream_eligible(kv_dtype, B, Hkv, block_size, max_blocks);
+    if (g_path == PA_PATH_STREAM) return ok ? pa_internal::kPathStream : 0;
+    return ok ? pa_internal::kPathStream : pa_internal::kPathPartition;
+}
+
 }  // namespace
 
 extern "C" {
@@ -96,11 +129,31 @@ int32_t pa_decode_partition_tokens(int32_t block_size, int32_t max_blocks) {
     return partition_tokens(block_size, max_blocks);
 }
 
-size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t block_size,
-                                 int32_t max_blocks) {
-    if (B <= 0 || Hq <= 0 || D <= 0 || block_size <= 0 || max_blocks <= 0) return 0;
+int32_t pa_set_decode_path(int32_t path) {
+    if (path != PA_PATH_AUTO && path != PA_PATH_PARTITION && path != PA_PATH_STREAM)
+        return fail(PA_ERR_INVALID_ARG, "decode path must be PA_PATH_AUTO, PA_PATH_PARTITION or PA_PATH_STREAM, got %d", path);
+    g_path = path;
+    return ok();
+}
+
+int32_t pa_set_stream_waves(int32_t waves, int32_t min_slice) {
+    if (waves < 0 || waves > pa_internal::kMaxStreamWaves || min_slice < 0 || min_slice > (1 << 20))
+        return fail(PA_ERR_INVALID_ARG, "stream waves must lie in [0, %d] and min_slice in [0, 2^20], got %d, %d",
+                    pa_internal::kMaxStreamWaves, waves, min_slice);
+    g_stream_waves = waves;
+    g_min_slice = min_slice == 0 ? pa_internal::kDefaultMinSlice : min_slice;
+    return ok();
+}
+
+size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                                 int32_t max_blocks, int32_t kv_dtype) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || block_size <= 0 || max_blocks <= 0)
+        return 0;
     size_t ml;
-    return workspace_layout(B, Hq, D, n_parts_for(block_size, max_blocks), &ml);
+    const size_t part = workspace_layout(B, Hq, D, n_parts_for(block_size, max_blocks), &ml);
+    const size_t strm = stream_eligible(kv_dtype, B, Hkv, block_size, max_blocks)
+                            ? stream_workspace(Hq / Hkv, D).total : 0;
+    return part > strm ? part : strm;
 }
 
 int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
@@ -138,12 +191,18 @@ int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_
         return fail(PA_ERR_INVALID_ARG, "pa_decode: misaligned pointer (q/out/caches need 16 bytes)");
     if ((int64_t)num_blocks * Hkv * block_size * D * elt_bytes(kv_dtype) < 0)
         return fail(PA_ERR_INVALID_ARG, "pa_decode: cache size overflows");
+    const int32_t path = choose_path(kv_dtype, B, Hkv, block_size, max_blocks);
+    if (path == 0)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: the stream path needs bf16 caches, B <= %d and "
+                    "fewer than 2^31 token groups", pa_internal::kMaxStreamB);
     const int32_t P = partition_tokens(block_size, max_blocks);
     if (P % block_size != 0)
         return fail(PA_ERR_INVALID_ARG, "pa_decode: partition %d not a multiple of block_size %d", P, block_size);
     const int32_t n_parts = n_parts_for(block_size, max_blocks);
     size_t ml_off = 0;
-    const size_t need = workspace_layout(B, Hq, D, n_parts, &ml_off);
+    const StreamWs sws = stream_workspace(G, D);
+    const size_t need = path == pa_internal::kPathStream ? sws.total
+                                                         : workspace_layout(B, Hq, D, n_parts, &ml_off);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return fail(PA_ERR_INVALID_ARG, "pa_decode: workspace of %zu bytes needed, %zu given",
@@ -151,14 +210,23 @@ int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_
         if (!aligned(workspace, 256))
             return fail(PA_ERR_INVALID_ARG, "pa_decode: workspace must be 256-byte aligned");
     }
-    if ((int64_t)n_parts * Hkv * B > 0x7fffffff)
+    if (path == pa_internal::kPathPartition && (int64_t)n_parts * Hkv * B > 0x7fffffff)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode: %lld work items exceed the grid limit",
                     (long long)n_parts * Hkv * B);
 
     pa_internal::DecodeLaunch a;
     a.out = out;
-    a.ws_o = need ? static_cast<float*>(workspace) : nullptr;
-    a.ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_off) : nullptr;
+    char* ws = static_cast<char*>(workspace);
+    const bool strm = path == pa_internal::kPathStream;
+    a.ws_o = (!strm && need) ? reinterpret_cast<float*>(ws) : nullptr;
+    a.ws_ml = (!strm && need) ? reinterpret_cast<float*>(ws + ml_off) : nullptr;
+    a.path = path;
+    a.rec_o = strm ? reinterpret_cast<float*>(ws) : nullptr;
+    a.rec_ml = strm ? reinterpret_cast<float*>(ws + sws.ml) : nullptr;
+    a.desc = strm ? reinterpret_cast<int32_t*>(ws + sws.desc) : nullptr;
+    a.meta = strm ? reinterpret_cast<int32_t*>(ws + sws.meta) : nullptr;
+    a.stream_waves = g_stream_waves;
+    a.min_slice = g_min_slice;
     a.q = q;
     a.k = k_cache;
     a.v = v_cache;

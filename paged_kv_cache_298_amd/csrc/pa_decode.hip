@@ -31,6 +31,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "pa_internal.h"
 
 // Build-time tuning knobs: ring depth (16-token groups in flight per wave) of the bf16 and
@@ -45,6 +47,12 @@
 #ifndef PA_BF16_QLDS
 #define PA_BF16_QLDS 0
 #endif
+#ifndef PA_BF16_WAVES
+#define PA_BF16_WAVES 4
+#endif
+#ifndef PA_STREAM_DEPTH
+#define PA_STREAM_DEPTH 4
+#endif
 #ifndef PA_DECODE_DEPTH
 #define PA_DECODE_DEPTH 4
 #endif
@@ -54,8 +62,14 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// s_waitcnt immediate for vmcnt(0) with the other counters left free (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVm0 = 0x0F70;
 
 struct Params {
     float* out;
@@ -68,6 +82,13 @@ struct Params {
     const int32_t* lens;
     int B, Hq, Hkv, bs, bs_shift, num_blocks, max_blocks, part_tokens, n_parts;
     float scale_log2;
+    // stream decomposition only
+    float* rec_o;     // [2 * nw, G, D] partial outputs of rows a wave covers only in part
+    float2* rec_ml;   // [2 * nw, G]    their (max in log2 units, sum)
+    int4* desc;       // [nw] first row of each wave's slice: b, g, row start, row groups
+    int* meta;        // [2] groups in the stream, waves given a slice
+    int nw;           // waves launched
+    int min_slice;    // fewest 16-token groups per wave
 };
 
 __device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u << 16); }
@@ -437,8 +458,8 @@ __device__ __forceinline__ float quad_bcast(float v, int m) {
     return __builtin_bit_cast(float, y);
 }
 
-template <int D, int G, int DEPTH, int kChunk, bool QLDS>
-__global__ __launch_bounds__(64) void decode_bf16_kernel(Params p) {
+template <int D, int G, int DEPTH, int kChunk, bool QLDS, int W>
+__global__ __launch_bounds__(64 * W) void decode_bf16_kernel(Params p) {
     constexpr int ROW = D * 2;              // bytes per cached row
     constexpr int NQ = D / 32;              // 16-byte registers per ring item
     constexpr int WV = D / 8;               // bytes of a V row per lane per load (16 or 8)
@@ -450,7 +471,8 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(Params p) {
     static_assert(D == 64 || D == 128, "head size");
     static_assert(kChunk % DEPTH == 0, "the ring depth must divide the chunk");
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave in the group
     int g, b, part;
     work_item(p, g, b, part);
     const int cap = p.max_blocks * p.bs;
@@ -458,28 +480,33 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(Params p) {
     L = L < 0 ? 0 : (L > cap ? cap : L);
     const int hq0 = g * G;
     const int t0 = part * p.part_tokens;
-    // The block-table slice of the partition is fetched before the sequence length is
-    // known (it does not depend on it): lane i holds entry i, clamped into the row and
-    // into the pool, and the loop reads it with v_readlane.
-    const int blk0 = t0 >> p.bs_shift;
+    // Wave wid takes the partition's 16-token groups wid, wid + W, wid + 2W, ... (its
+    // "local" groups 0, 1, 2, ...). The block-table entries of those groups are fetched
+    // before the sequence length is known (they do not depend on it): lane i holds the
+    // entry of local group i, clamped into the row and into the pool, and the loop reads
+    // it with v_readlane.
     int tblv;
     {
         const int32_t* trow = p.tables + (int64_t)b * p.max_blocks;
-        int i = blk0 + lane;
+        int i = (t0 + (wid + lane * W) * 16) >> p.bs_shift;
         i = i < p.max_blocks ? i : p.max_blocks - 1;
         const int e = trow[i];
         tblv = e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);
     }
     if (t0 >= L) {
         if (part == 0) {   // empty sequence: a zero row per head
-            for (int i = lane; i < G * D; i += 64)
+            for (int i = threadIdx.x; i < G * D; i += 64 * W)
                 p.out[((int64_t)b * p.Hq + hq0) * D + i] = 0.f;
         }
         return;
     }
-    const int ntok = min(p.part_tokens, L - t0);
-    const int ngroups = (ntok + 15) >> 4;
+    const int ntok_part = min(p.part_tokens, L - t0);
+    const int ng_part = (ntok_part + 15) >> 4;
+    // this wave's stream: ngroups local groups, all full but possibly the last, which
+    // holds the partition's final tokens; ntok counts the stream's tokens
+    const int ngroups = ng_part > wid ? (ng_part - wid + W - 1) / W : 0;
     const int last = ngroups - 1;
+    const int ntok = ngroups > 0 ? last * 16 + min(16, ntok_part - (wid + last * W) * 16) : 0;
     const int nchunks = (ngroups + kChunk - 1) / kChunk;
     const int nparts_b = (L + p.part_tokens - 1) / p.part_tokens;
 
@@ -525,8 +552,9 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(Params p) {
         const bool is_v = t >= kChunk;
         int gi = ch * kChunk + (is_v ? t - kChunk : t);
         gi = gi < last ? gi : last;
-        const int ph = __builtin_amdgcn_readlane(tblv, (gi << 4) >> p.bs_shift);
-        const int64_t off = (int64_t)ph * blk_bytes + (int64_t)((gi << 4) & bs_mask) * ROW;
+        const int ph = __builtin_amdgcn_readlane(tblv, gi);
+        const int tok = t0 + (wid + gi * W) * 16;
+        const int64_t off = (int64_t)ph * blk_bytes + (int64_t)(tok & bs_mask) * ROW;
         if (!is_v) {
             const char* kb = kbase + off;
 #pragma unroll
@@ -566,8 +594,6 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(Params p) {
     const float cl2 = p.scale_log2;
 
     Item ring[DEPTH];
-#pragma unroll
-    for (int j = 0; j < DEPTH; ++j) issue(0, j, ring[j]);
 
     // One chunk: consume its 2 * kChunk stream items in order, refilling each ring slot
     // with the item DEPTH positions later. `masked` (the last chunk only) handles tokens
@@ -673,8 +699,12 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(Params p) {
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    for (int ch = 0; ch < nchunks - 1; ++ch) chunk(ch, false);
-    chunk(nchunks - 1, true);
+    if (ngroups > 0) {
+#pragma unroll
+        for (int j = 0; j < DEPTH; ++j) issue(0, j, ring[j]);
+        for (int ch = 0; ch < nchunks - 1; ++ch) chunk(ch, false);
+        chunk(nchunks - 1, true);
+    }
 
     // add the four row groups' partial sums (lanes c, c + 16, c + 32, c + 48)
 #pragma unroll
@@ -695,31 +725,79 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(Params p) {
             lh[s][m] = quad_bcast(l_run[s], m);
             mh[s][m] = quad_bcast(m_run[s], m);
         }
-    if (r == 0) {
+    if constexpr (W == 1) {
+        if (r == 0) {
 #pragma unroll
-        for (int s = 0; s < NSET; ++s) {
+            for (int s = 0; s < NSET; ++s) {
 #pragma unroll
-            for (int m = 0; m < G4; ++m) {
-                const int h = 4 * s + m;
-                float o[EV];
+                for (int m = 0; m < G4; ++m) {
+                    const int h = 4 * s + m;
+                    float o[EV];
 #pragma unroll
-                for (int e = 0; e < EV; ++e) o[e] = acc[s][e][m];
-                if (nparts_b == 1) {
-                    const float inv = 1.0f / lh[s][m];
-                    float* dst = p.out + ((int64_t)b * p.Hq + hq0 + h) * D + c * EV;
+                    for (int e = 0; e < EV; ++e) o[e] = acc[s][e][m];
+                    if (nparts_b == 1) {
+                        const float inv = 1.0f / lh[s][m];
+                        float* dst = p.out + ((int64_t)b * p.Hq + hq0 + h) * D + c * EV;
 #pragma unroll
-                    for (int e = 0; e < EV; e += 4)
-                        *reinterpret_cast<float4*>(dst + e) =
-                            make_float4(o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv);
-                } else {
-                    float* dst = p.ws_o + (((int64_t)b * p.Hq + hq0 + h) * p.n_parts + part) * D + c * EV;
+                        for (int e = 0; e < EV; e += 4)
+                            *reinterpret_cast<float4*>(dst + e) =
+                                make_float4(o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv);
+                    } else {
+                        float* dst = p.ws_o + (((int64_t)b * p.Hq + hq0 + h) * p.n_parts + part) * D + c * EV;
 #pragma unroll
-                    for (int e = 0; e < EV; e += 4)
-                        *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
-                    if (c == 0)
-                        p.ws_ml[((int64_t)b * p.Hq + hq0 + h) * p.n_parts + part] =
-                            make_float2(mh[s][m], lh[s][m]);
+                        for (int e = 0; e < EV; e += 4)
+                            *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+                        if (c == 0)
+                            p.ws_ml[((int64_t)b * p.Hq + hq0 + h) * p.n_parts + part] =
+                                make_float2(mh[s][m], lh[s][m]);
+                    }
                 }
+            }
+        }
+    } else {
+        // the W waves' partial states meet in LDS; every thread of the group then
+        // combines one float4 of the G x D output exactly like the split reduce does
+        __shared__ float4 o_lds[W][G][D / 4];
+        __shared__ float2 ml_lds[W][G];
+        if (r == 0) {
+#pragma unroll
+            for (int s = 0; s < NSET; ++s) {
+#pragma unroll
+                for (int m = 0; m < G4; ++m) {
+                    const int h = 4 * s + m;
+#pragma unroll
+                    for (int e = 0; e < EV; e += 4)
+                        o_lds[wid][h][(c * EV + e) / 4] =
+                            make_float4(acc[s][e][m], acc[s][e + 1][m], acc[s][e + 2][m], acc[s][e + 3][m]);
+                    if (c == 0) ml_lds[wid][h] = make_float2(mh[s][m], lh[s][m]);
+                }
+            }
+        }
+        __syncthreads();
+        constexpr int C4 = D / 4;
+        for (int i = threadIdx.x; i < G * C4; i += 64 * W) {
+            const int h = i / C4, c4 = i % C4;
+            float M = -INFINITY;
+#pragma unroll
+            for (int v = 0; v < W; ++v) M = fmaxf(M, ml_lds[v][h].x);
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+            float ls = 0.f;
+#pragma unroll
+            for (int v = 0; v < W; ++v) {
+                const float2 ml = ml_lds[v][h];
+                const float wgt = __builtin_amdgcn_exp2f(ml.x - M);   // 0 for an idle wave
+                const float4 x = o_lds[v][h][c4];
+                o.x += wgt * x.x; o.y += wgt * x.y; o.z += wgt * x.z; o.w += wgt * x.w;
+                ls += wgt * ml.y;
+            }
+            const int64_t row = (int64_t)b * p.Hq + hq0 + h;
+            if (nparts_b == 1) {
+                const float inv = 1.0f / ls;
+                reinterpret_cast<float4*>(p.out + row * D)[c4] =
+                    make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+            } else {
+                reinterpret_cast<float4*>(p.ws_o + (row * p.n_parts + part) * D)[c4] = o;
+                if (c4 == 0) p.ws_ml[row * p.n_parts + part] = make_float2(M, ls);
             }
         }
     }
@@ -788,12 +866,464 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
 
 
 
+
+// ---------------------------------------------------------------------------------------
+// Stream decomposition (bf16 KV). The rows (sequence b, KV head g), each cut into
+// ceil(L_b / 16) groups of 16 tokens, are laid end to end into one stream of T groups,
+// and each of nw resident waves takes an equal contiguous slice of it. A wave walks its
+// slice with one load ring that never drains between rows: it finishes rows it covers
+// whole by writing the output directly, and leaves a partial state (max, sum, unscaled
+// output) for the at most two rows it covers only in part; stream_reduce_kernel merges
+// those. Each group's K tile and V tile are 4 KiB items of the ring; the online softmax
+// is updated once per group. Block-table lookups for 64 groups at a time ("window") are
+// resolved lane-parallel: lane i finds the row of group sw + i by a binary search over
+// the per-sequence prefix of group counts kept in LDS, then gathers its table entry.
+template <int D, int G, int DEPTH>
+__global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
+    constexpr int ROW = D * 2;              // bytes per cached row
+    constexpr int NQ = D / 32;              // 16-byte registers per ring item
+    constexpr int WV = D / 8;               // bytes of a V row per lane per load (16 or 8)
+    constexpr int EV = D / 16;              // bf16 elements per lane per V load
+    constexpr int NSET = (G + 3) / 4;       // head sets of 4
+    constexpr int G4 = G < 4 ? G : 4;       // distinct heads in a set
+    constexpr int U = DEPTH / 2;            // groups in flight ahead of the consumer
+    static_assert(D == 64 || D == 128, "head size");
+    static_assert(DEPTH >= 2 && DEPTH % 2 == 0, "ring holds whole groups (K and V)");
+
+    extern __shared__ int lds_prefix[];
+    int* Cs = lds_prefix;           // [B + 1] exclusive prefix of groups per sequence
+    int* Ls = lds_prefix + p.B + 1; // [B] lengths clamped into the table's capacity
+    __shared__ int wsum[4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cap = p.max_blocks * p.bs;
+
+    // ---- groups per sequence and their exclusive prefix over the batch (whole block)
+    const int per = (p.B + 255) >> 8;
+    int loc = 0;
+    for (int i = 0; i < per; ++i) {
+        const int bb = tid * per + i;
+        if (bb < p.B) {
+            int L = p.lens[bb];
+            L = L < 0 ? 0 : (L > cap ? cap : L);
+            Ls[bb] = L;
+            loc += (L + 15) >> 4;
+        }
+    }
+    int inc = loc;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(inc, d);
+        if (lane >= d) inc += y;
+    }
+    if (lane == 63) wsum[wid] = inc;
+    __syncthreads();
+    int run = inc - loc;
+    for (int v = 0; v < wid; ++v) run += wsum[v];
+    for (int i = 0; i < per; ++i) {
+        const int bb = tid * per + i;
+        if (bb < p.B) {
+            Cs[bb] = run;
+            run += (Ls[bb] + 15) >> 4;
+        }
+    }
+    if (tid == 255) Cs[p.B] = run;
+    __syncthreads();
+
+    const int T = __builtin_amdgcn_readfirstlane(Cs[p.B]) * p.Hkv;
+    const int gw = blockIdx.x * 4 + wid;
+    int nwe = T / p.min_slice;
+    nwe = nwe < 1 ? 1 : (nwe > p.nw ? p.nw : nwe);
+    if (T == 0) nwe = 0;
+    if (gw == 0 && lane == 0) {
+        p.meta[0] = T;
+        p.meta[1] = nwe;
+    }
+    // empty sequences: a zero row per query head
+    for (int bb = gw; bb < p.B; bb += p.nw) {
+        if (__builtin_amdgcn_readfirstlane(Ls[bb]) == 0) {
+            float* o = p.out + (int64_t)bb * p.Hq * D;
+            for (int i = lane; i < p.Hq * D; i += 64) o[i] = 0.f;
+        }
+    }
+    if (gw >= nwe) return;
+    const int s0 = (int)((int64_t)gw * T / nwe);
+    const int s1 = (int)((int64_t)(gw + 1) * T / nwe);
+    const int ns = s1 - s0;
+
+    const int64_t tile_bytes = (int64_t)p.bs * ROW;              // one (block, head) tile
+    const int64_t blk_bytes = (int64_t)p.Hkv * tile_bytes;       // one physical block
+    const int bs_mask = p.bs - 1;
+
+    // ---- window: lane i describes group sw + i of the slice (clamped into it)
+    uint32_t w_lo = 0, w_hi = 0;   // byte offset of the group's tile in either cache
+    int w_row = 0, w_j = 0;        // its row (b * Hkv + g) and group within the row
+    int sw = s0;
+    auto window = [&](int base) {
+        int s = base + lane;
+        s = s < s1 ? s : s1 - 1;
+        int lo = 0, hi = p.B - 1;
+        while (lo < hi) {           // first sequence whose groups end past s
+            const int mid = (lo + hi) >> 1;
+            if (Cs[mid + 1] * p.Hkv > s) hi = mid;
+            else lo = mid + 1;
+        }
+        const int n = Cs[lo + 1] - Cs[lo];
+        const int off = s - Cs[lo] * p.Hkv;
+        const int g = off / n;
+        const int j = off - g * n;
+        int e = p.tables[(int64_t)lo * p.max_blocks + ((j << 4) >> p.bs_shift)];
+        e = e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);
+        const int64_t o = (int64_t)e * blk_bytes + (int64_t)g * tile_bytes +
+                          (int64_t)((j << 4) & bs_mask) * ROW;
+        w_lo = (uint32_t)o;
+        w_hi = (uint32_t)((uint64_t)o >> 32);
+        w_row = lo * p.Hkv + g;
+        w_j = j;
+    };
+    window(sw);
+
+    // ---- consumer cursor (wave-uniform, kept in scalar registers): sequence, KV head,
+    // group in row, groups in row, tokens in row. Lengths are re-read through the scalar
+    // cache so that no vector register enters the cursor's updates.
+    typedef __attribute__((address_space(4))) const int32_t* const_i32p;
+    const const_i32p slens = (const_i32p)(p.lens);
+    auto seq_len = [&](int bb) -> int {
+        const int L = slens[bb];
+        return L < 0 ? 0 : (L > cap ? cap : L);
+    };
+    const int row0 = __builtin_amdgcn_readlane(w_row, 0);
+    int cb = row0 / p.Hkv;
+    int cg = row0 - cb * p.Hkv;
+    int cj = __builtin_amdgcn_readlane(w_j, 0);
+    int cL = seq_len(cb);
+    int cn = (cL + 15) >> 4;
+    if (lane == 0) p.desc[gw] = make_int4(cb, cg, s0 - cj, cn);
+
+    const int r = lane >> 4;     // row group
+    const int c = lane & 15;     // column
+    // query fragments of the current row and of the next row the loads reach
+    u32x4_t qf[NSET][NQ], qn[NSET][NQ];
+    auto load_q = [&](int row, u32x4_t (&dst)[NSET][NQ]) {
+        const int bq = row / p.Hkv;
+        const int gq = row - bq * p.Hkv;
+#pragma unroll
+        for (int s = 0; s < NSET; ++s) {
+            const int h = 4 * s + ((c & 3) % G4);
+            const char* qrow = p.q + ((int64_t)bq * p.Hq + gq * G + h) * ROW;
+#pragma unroll
+            for (int k = 0; k < NQ; ++k)
+                dst[s][k] = *reinterpret_cast<const u32x4_t*>(qrow + (k * 32 + r * 8) * 2);
+        }
+    };
+    load_q(row0, qf);
+#pragma unroll
+    for (int s = 0; s < NSET; ++s)
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) qn[s][k] = qf[s][k];
+    int qn_row = -1;       // row whose fragments sit in qn
+    int iss_row = row0;    // row of the last K tile issued
+
+    const uint32_t koff = (uint32_t)(((c >> 2) + 4 * (c & 3)) * ROW + r * 16);
+    const uint32_t voff = (uint32_t)(r * ROW + c * WV);
+    struct Item {
+        u32x4_t q[NQ];
+    };
+    auto tile_off = [&](int gq) -> uint64_t {
+        int s = s0 + gq;
+        s = s < s1 ? s : s1 - 1;
+        if (s - sw >= 64) {
+            sw += 64;
+            window(sw);
+        }
+        const int idx = s - sw;
+        return ((uint64_t)__builtin_amdgcn_readlane(w_hi, idx) << 32) |
+               (uint64_t)__builtin_amdgcn_readlane(w_lo, idx);
+    };
+    auto issue_k = [&](int gq, Item& dst) {
+        const uint64_t off = tile_off(gq);
+        int s = s0 + gq;
+        s = s < s1 ? s : s1 - 1;
+        const int row = __builtin_amdgcn_readlane(w_row, s - sw);
+        if (row != iss_row) {       // the loads enter a new row: fetch its query early
+            iss_row = row;
+            qn_row = row;
+            load_q(row, qn);
+        }
+        const char* kb = p.k + off;
+#pragma unroll
+        for (int k = 0; k < NQ; ++k)
+            dst.q[k] = *reinterpret_cast<const u32x4_t*>(kb + koff + k * 64);
+    };
+    auto issue_v = [&](int gq, Item& dst) {
+        const char* vb = p.v + tile_off(gq);
+        if constexpr (WV == 16) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                dst.q[k] = *reinterpret_cast<const u32x4_t*>(vb + voff + k * 4 * ROW);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; k += 2) {
+                const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vb + voff + k * 4 * ROW);
+                const u32x2_t e = *reinterpret_cast<const u32x2_t*>(vb + voff + (k + 1) * 4 * ROW);
+                dst.q[k / 2] = __builtin_shufflevector(a, e, 0, 1, 2, 3);
+            }
+        }
+    };
+    auto vword = [&](const Item& it, int k, int w) -> uint32_t {
+        if constexpr (WV == 16) return it.q[k][w];
+        else return it.q[k >> 1][(k & 1) * 2 + w];
+    };
+
+    f32x4_t acc[NSET][EV];
+    float m_run[NSET], l_run[NSET];
+    auto reset = [&]() {
+#pragma unroll
+        for (int s = 0; s < NSET; ++s) {
+            m_run[s] = -INFINITY;
+            l_run[s] = 0.f;
+#pragma unroll
+            for (int e = 0; e < EV; ++e) acc[s][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    reset();
+    bool first_seg = true;   // the slice's first row segment
+    int seg_j0 = cj;         // first group of the current row segment
+    const float cl2 = p.scale_log2;
+
+    // write the state of the current row segment: the output if the segment is the whole
+    // row, else a partial record (slot 0: the slice's first segment, slot 1: its last)
+    auto flush = [&]() {
+        const bool whole = seg_j0 == 0 && cj == cn - 1;
+        float lh[NSET][4], mh[NSET][4];
+#pragma unroll
+        for (int s = 0; s < NSET; ++s) {
+            l_run[s] = rows_sum(l_run[s]);   // the output tile needs no sum: rows repeat
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                lh[s][m] = quad_bcast(l_run[s], m);
+                mh[s][m] = quad_bcast(m_run[s], m);
+            }
+        }
+        if (r == 0) {
+            const int rec = 2 * gw + (first_seg ? 0 : 1);
+#pragma unroll
+            for (int s = 0; s < NSET; ++s) {
+#pragma unroll
+                for (int m = 0; m < G4; ++m) {
+                    const int h = 4 * s + m;
+                    if (whole) {
+                        const float inv = 1.0f / lh[s][m];
+                        float* dst = p.out + ((int64_t)cb * p.Hq + cg * G + h) * D + c * EV;
+#pragma unroll
+                        for (int e = 0; e < EV; e += 4)
+                            *reinterpret_cast<float4*>(dst + e) =
+                                make_float4(acc[s][e][m] * inv, acc[s][e + 1][m] * inv,
+                                            acc[s][e + 2][m] * inv, acc[s][e + 3][m] * inv);
+                    } else {
+                        float* dst = p.rec_o + ((int64_t)rec * G + h) * D + c * EV;
+#pragma unroll
+                        for (int e = 0; e < EV; e += 4)
+                            *reinterpret_cast<float4*>(dst + e) =
+                                make_float4(acc[s][e][m], acc[s][e + 1][m], acc[s][e + 2][m], acc[s][e + 3][m]);
+                        if (c == 0) p.rec_ml[(int64_t)rec * G + h] = make_float2(mh[s][m], lh[s][m]);
+                    }
+                }
+            }
+        }
+    };
+
+    Item ring[DEPTH];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {   // fill the ring in stream order (the waits count on it)
+        __builtin_amdgcn_sched_barrier(0);
+        issue_k(u, ring[2 * u]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_v(u, ring[2 * u + 1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int t0 = 0; t0 < ns; t0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = t0 + u;
+            Item& kit = ring[2 * u];
+            Item& vit = ring[2 * u + 1];
+            const bool live = t < ns;
+            const int valid = min(16, cL - 16 * cj);   // tokens of the group (last may be short)
+            float y[NSET][4];
+            uint32_t pw[NSET][2];   // bf16 probabilities of tokens r + 4i, two per dword
+            if (live) {
+                // ---- scores of the group on the matrix cores, in log2 units
+#pragma unroll
+                for (int s = 0; s < NSET; ++s) {
+                    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int k = 0; k < NQ; ++k)
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, kit.q[k]),
+                            __builtin_bit_cast(bf16x8_t, qf[s][k]), sc, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y[s][i] = sc[i] * cl2;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            issue_k(t + U, kit);
+            __builtin_amdgcn_sched_barrier(0);
+            if (live) {
+                // ---- online softmax update: lane holds tokens r + 4i of head column c
+#pragma unroll
+                for (int s = 0; s < NSET; ++s) {
+                    if (valid < 16) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) y[s][i] = (r + 4 * i < valid) ? y[s][i] : -INFINITY;
+                    }
+                    const float mx = fmaxf(fmaxf(y[s][0], y[s][1]), fmaxf(y[s][2], y[s][3]));
+                    const float m_new = fmaxf(m_run[s], rows_max(mx));
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_new);
+                    m_run[s] = m_new;
+                    float am[4];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) am[m] = quad_bcast(alpha, m);
+#pragma unroll
+                    for (int e = 0; e < EV; ++e)
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) acc[s][e][m] *= am[m];
+                    // probabilities, rounded to bf16 for the matrix cores; the sum takes
+                    // the rounded values too, so the weights it divides by are the ones used
+                    const bf16x2_t p01 = __builtin_convertvector(
+                        (f32x2_t){__builtin_amdgcn_exp2f(y[s][0] - m_new), __builtin_amdgcn_exp2f(y[s][1] - m_new)}, bf16x2_t);
+                    const bf16x2_t p23 = __builtin_convertvector(
+                        (f32x2_t){__builtin_amdgcn_exp2f(y[s][2] - m_new), __builtin_amdgcn_exp2f(y[s][3] - m_new)}, bf16x2_t);
+                    pw[s][0] = __builtin_bit_cast(uint32_t, p01);
+                    pw[s][1] = __builtin_bit_cast(uint32_t, p23);
+                    l_run[s] = l_run[s] * alpha + ((lo_bf16(pw[s][0]) + hi_bf16(pw[s][0])) +
+                                                   (lo_bf16(pw[s][1]) + hi_bf16(pw[s][1])));
+                }
+                // ---- o += p * V on the matrix cores; V rows past the end may hold anything
+                if (valid < 16) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        if (r + 4 * k >= valid) {
+                            if constexpr (WV == 16) {
+                                vit.q[k] = u32x4_t{0u, 0u, 0u, 0u};
+                            } else {
+                                vit.q[k >> 1][(k & 1) * 2] = 0u;
+                                vit.q[k >> 1][(k & 1) * 2 + 1] = 0u;
+                            }
+                        }
+                    }
+                }
+                // One v_mfma_f32_16x16x16_bf16 per output column set e: A = the lane's four
+                // probabilities (row = head column c, k = tokens r + 4i, exactly as the score
+                // tile left them), B = V[r + 4i][c * EV + e], gathered from the four V loads
+                // with byte permutes. Output rows 4r..4r+3 repeat the G4 heads for every r.
+#pragma unroll
+                for (int w = 0; w < WV / 4; ++w) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+                        const u32x2_t bv = {__builtin_amdgcn_perm(vword(vit, 1, w), vword(vit, 0, w), sel),
+                                            __builtin_amdgcn_perm(vword(vit, 3, w), vword(vit, 2, w), sel)};
+#pragma unroll
+                        for (int s = 0; s < NSET; ++s) {
+                            const u32x2_t av = {pw[s][0], pw[s][1]};
+                            acc[s][2 * w + h] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                                __builtin_bit_cast(s16x4_t, av), __builtin_bit_cast(s16x4_t, bv),
+                                acc[s][2 * w + h], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            issue_v(t + U, vit);
+            __builtin_amdgcn_sched_barrier(0);
+            if (live) {
+                const bool seg_end = cj == cn - 1 || t == ns - 1;
+                const int cj_next = seg_end ? 0 : cj + 1;   // defined on every path
+                if (seg_end) {
+                    flush();
+                    if (t < ns - 1) {     // the slice goes on into the next row
+                        ++cg;
+                        if (cg == p.Hkv) {
+                            cg = 0;
+                            do {   // skip empty sequences (bounded by the batch)
+                                cL = seq_len(++cb);
+                            } while (cL == 0 && cb < p.B - 1);
+                        }
+                        cn = (cL + 15) >> 4;
+                        seg_j0 = 0;
+                        first_seg = false;
+                        const int row = cb * p.Hkv + cg;
+                        // The prefetched fragments are copied (the compiler waits for
+                        // exactly their loads); fragments loaded here are waited for at
+                        // once (a rare case), so that past this point the query
+                        // registers hold no pending load on any path and the ring's
+                        // waits stay exact.
+                        if (qn_row == row) {
+#pragma unroll
+                            for (int s = 0; s < NSET; ++s)
+#pragma unroll
+                                for (int k = 0; k < NQ; ++k) qf[s][k] = qn[s][k];
+                        } else {
+                            load_q(row, qf);
+                            __builtin_amdgcn_s_waitcnt(kWaitVm0);
+                        }
+                        reset();
+                    }
+                }
+                cj = cj_next;
+            }
+        }
+    }
+}
+
+// Merge the partial records of rows that cross slice boundaries. Group w looks at the
+// row holding the first group of slice w; it merges it only when that row began inside
+// slice w - 1, so every split row is merged exactly once, records in slice order.
+template <int D, int G>
+__global__ __launch_bounds__(256) void stream_reduce_kernel(Params p) {
+    constexpr int C4 = D / 4;
+    const int w = blockIdx.x;
+    const int T = p.meta[0];
+    const int nwe = p.meta[1];
+    if (w == 0 || w >= nwe) return;
+    const int4 d = p.desc[w];          // b, g, row start, row groups
+    const int s0w = (int)((int64_t)w * T / nwe);
+    if (d.z >= s0w) return;            // the row starts in slice w: not split here
+    const int s0p = (int)((int64_t)(w - 1) * T / nwe);
+    if (d.z < s0p) return;             // began before slice w - 1: merged by an earlier group
+    const int last = d.z + d.w - 1;
+    const int wb = (int)(((int64_t)(last + 1) * nwe - 1) / T);   // slice holding the last group
+    const int rec_a = 2 * (w - 1) + (d.z == s0p ? 0 : 1);
+    for (int i = threadIdx.x; i < G * C4; i += 256) {
+        const int h = i / C4, c4 = i % C4;
+        float M = p.rec_ml[(int64_t)rec_a * G + h].x;
+        for (int x = w; x <= wb; ++x) M = fmaxf(M, p.rec_ml[(int64_t)(2 * x) * G + h].x);
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        float l = 0.f;
+        for (int x = w - 1; x <= wb; ++x) {
+            const int rec = x == w - 1 ? rec_a : 2 * x;
+            const float2 ml = p.rec_ml[(int64_t)rec * G + h];
+            const float wgt = __builtin_amdgcn_exp2f(ml.x - M);
+            const float4 v = reinterpret_cast<const float4*>(p.rec_o + ((int64_t)rec * G + h) * D)[c4];
+            o.x += wgt * v.x; o.y += wgt * v.y; o.z += wgt * v.z; o.w += wgt * v.w;
+            l += wgt * ml.y;
+        }
+        const float inv = 1.0f / l;
+        reinterpret_cast<float4*>(p.out + ((int64_t)d.x * p.Hq + d.y * G + h) * D)[c4] =
+            make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    }
+}
+
 template <bool BF16, int D, int G>
 hipError_t launch_one(const Params& prm, int B, int Hkv, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if constexpr (BF16) {
-        hipLaunchKernelGGL((decode_bf16_kernel<D, G, PA_BF16_DEPTH, PA_BF16_CHUNK, (PA_BF16_QLDS != 0)>), dim3(prm.n_parts * Hkv * B),
-                           dim3(64), 0, s, prm);
+        hipLaunchKernelGGL((decode_bf16_kernel<D, G, PA_BF16_DEPTH, PA_BF16_CHUNK, (PA_BF16_QLDS != 0), PA_BF16_WAVES>),
+                           dim3(prm.n_parts * Hkv * B), dim3(64 * PA_BF16_WAVES), 0, s, prm);
     } else {
         const size_t lds = (size_t)prm.part_tokens * G * sizeof(float) +
                            (size_t)(prm.part_tokens / 16) * sizeof(int);
@@ -803,6 +1333,70 @@ hipError_t launch_one(const Params& prm, int B, int Hkv, void* stream) {
     if (prm.n_parts > 1)
         hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(prm.Hq, B), dim3(256), 0, s, prm);
     return hipGetLastError();
+}
+
+// Waves of the stream kernel that the device holds at once (cached per device, kernel and
+// LDS size).
+int resident_waves(const void* kern, size_t lds, int* nw) {
+    struct Entry {
+        int dev;
+        const void* kern;
+        size_t lds;
+        int nw;
+    };
+    static std::mutex mu;
+    static Entry cache[16];
+    static int used = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < used; ++i)
+            if (cache[i].dev == dev && cache[i].kern == kern && cache[i].lds == lds) {
+                *nw = cache[i].nw;
+                return 0;
+            }
+    }
+    int cus = 0, nb = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return (int)e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 256, lds);
+    if (e != hipSuccess) return (int)e;
+    if (nb < 1) return (int)hipErrorInvalidConfiguration;
+    *nw = cus * nb * 4;
+    std::lock_guard<std::mutex> lock(mu);
+    if (used < 16) cache[used++] = Entry{dev, kern, lds, *nw};
+    return 0;
+}
+
+template <int D, int G>
+hipError_t launch_stream(Params prm, int nw_req, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const size_t lds = (size_t)(2 * prm.B + 1) * sizeof(int);
+    const void* kern = reinterpret_cast<const void*>(&decode_stream_kernel<D, G, PA_STREAM_DEPTH>);
+    int nw = nw_req;
+    if (nw <= 0) {
+        const int e = resident_waves(kern, lds, &nw);
+        if (e != 0) return (hipError_t)e;
+    }
+    nw = nw > pa_internal::kMaxStreamWaves ? pa_internal::kMaxStreamWaves : nw;
+    nw = (nw + 3) / 4 * 4;
+    prm.nw = nw;
+    hipLaunchKernelGGL((decode_stream_kernel<D, G, PA_STREAM_DEPTH>), dim3(nw / 4), dim3(256), lds, s, prm);
+    hipLaunchKernelGGL((stream_reduce_kernel<D, G>), dim3(nw), dim3(256), 0, s, prm);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch_stream_g(const Params& prm, int G, int nw, void* stream) {
+    switch (G) {
+        case 1: return launch_stream<D, 1>(prm, nw, stream);
+        case 2: return launch_stream<D, 2>(prm, nw, stream);
+        case 4: return launch_stream<D, 4>(prm, nw, stream);
+        case 8: return launch_stream<D, 8>(prm, nw, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <bool BF16, int D>
@@ -850,10 +1444,23 @@ int launch_decode(const DecodeLaunch& a, const char** err) {
     prm.n_parts = a.n_parts;
     prm.scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     (void)kLog2e;
+    prm.rec_o = a.rec_o;
+    prm.rec_ml = reinterpret_cast<float2*>(a.rec_ml);
+    prm.desc = reinterpret_cast<int4*>(a.desc);
+    prm.meta = a.meta;
+    prm.nw = 0;
+    prm.min_slice = a.min_slice > 0 ? a.min_slice : 1;
     if (a.B == 0) return 0;
     const int G = a.Hq / a.Hkv;
-    hipError_t e = a.kv_dtype == 1 ? dispatch_d<true>(prm, a.B, a.Hkv, a.D, G, a.stream)
-                                   : dispatch_d<false>(prm, a.B, a.Hkv, a.D, G, a.stream);
+    hipError_t e;
+    if (a.path == kPathStream) {
+        e = a.D == 64 ? dispatch_stream_g<64>(prm, G, a.stream_waves, a.stream)
+          : a.D == 128 ? dispatch_stream_g<128>(prm, G, a.stream_waves, a.stream)
+                       : hipErrorInvalidValue;
+    } else {
+        e = a.kv_dtype == 1 ? dispatch_d<true>(prm, a.B, a.Hkv, a.D, G, a.stream)
+                            : dispatch_d<false>(prm, a.B, a.Hkv, a.D, G, a.stream);
+    }
     if (e != hipSuccess) {
         *err = hipGetErrorString(e);
         return (int)e;

@@ -23,10 +23,23 @@ struct DecodeLaunch {
     int32_t kv_dtype;        // PA_F32 / PA_BF16
     float scale;
     void* stream;
+    // stream decomposition (path == kPathStream)
+    int32_t path;            // kPathPartition or kPathStream
+    float* rec_o;            // [2 * kMaxStreamWaves, G, D]
+    float* rec_ml;           // [2 * kMaxStreamWaves, G, 2]
+    int32_t* desc;           // [kMaxStreamWaves, 4]
+    int32_t* meta;           // [4]
+    int32_t stream_waves;    // 0 = every wave the device holds at once
+    int32_t min_slice;       // fewest 16-token groups per wave
 };
 
 constexpr int kMaxPartTokens = 1024;
-constexpr int kDefaultPartTokens = 256;
+constexpr int kDefaultPartTokens = 512;
+constexpr int kPathPartition = 1;
+constexpr int kPathStream = 2;
+constexpr int kMaxStreamB = 4096;        // sequences whose prefix fits the kernel's LDS
+constexpr int kMaxStreamWaves = 4096;    // resident waves the records are sized for
+constexpr int kDefaultMinSlice = 8;
 
 // Each returns 0 on success or a nonzero HIP error code (message in *err).
 int launch_decode(const DecodeLaunch& a, const char** err);

@@ -18,6 +18,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 PA_F32, PA_BF16 = 0, 1
+PA_PATH_AUTO, PA_PATH_PARTITION, PA_PATH_STREAM = 0, 1, 2
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS, PA_ERR_HIP = 0, -1, -2, -3, -4
 
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -26,9 +27,11 @@ _P32 = ctypes.POINTER(ctypes.c_int32)
 _SIGS = {
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _f32, _i32, _vp, _sz, _vp]),
-    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_partition_tokens": (_i32, [_i32, _i32]),
     "pa_set_partition_tokens": (_i32, [_i32]),
+    "pa_set_decode_path": (_i32, [_i32]),
+    "pa_set_stream_waves": (_i32, [_i32, _i32]),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                     _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
@@ -93,8 +96,8 @@ def abi_version():
     return int(_lib.pa_abi_version())
 
 
-def pa_decode_workspace_bytes(B, Hq, D, block_size, max_blocks):
-    return int(_lib.pa_decode_workspace_bytes(B, Hq, D, block_size, max_blocks))
+def pa_decode_workspace_bytes(B, Hq, Hkv, D, block_size, max_blocks, kv_dtype):
+    return int(_lib.pa_decode_workspace_bytes(B, Hq, Hkv, D, block_size, max_blocks, kv_dtype))
 
 
 def pa_decode_partition_tokens(block_size, max_blocks):
@@ -103,6 +106,14 @@ def pa_decode_partition_tokens(block_size, max_blocks):
 
 def pa_set_partition_tokens(tokens):
     _check(_lib.pa_set_partition_tokens(int(tokens)))
+
+
+def pa_set_decode_path(path):
+    _check(_lib.pa_set_decode_path(int(path)))
+
+
+def pa_set_stream_waves(waves, min_slice=0):
+    _check(_lib.pa_set_stream_waves(int(waves), int(min_slice)))
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, workspace=None,
@@ -114,7 +125,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, workspace
     B, Hq, D = q.shape
     nb, Hkv, bs, _ = k_cache.shape
     max_blocks = block_tables.shape[1]
-    need = pa_decode_workspace_bytes(B, Hq, D, bs, max_blocks)
+    need = pa_decode_workspace_bytes(B, Hq, Hkv, D, bs, max_blocks, _kv_dtype(k_cache))
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

@@ -31,7 +31,7 @@ def test_header_declarations_are_all_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert pa.abi_version() == 1
+    assert pa.abi_version() == 2
     for code, name in [(0, "PA_OK"), (-1, "PA_ERR_INVALID_ARG"), (-2, "PA_ERR_UNSUPPORTED"),
                        (-3, "PA_ERR_NO_BLOCKS"), (-4, "PA_ERR_HIP")]:
         assert pa._lib.pa_status_string(code).decode() == name
@@ -72,26 +72,70 @@ def test_decode_empty_batch_is_a_no_op():
     assert _decode(B=0, out=None, q=None) == pa.PA_OK
 
 
+def _up(x):
+    return (x + 255) // 256 * 256
+
+
+def _stream_ws(G, D, waves=4096):
+    """Record layout of the stream decomposition: partial outputs, (max, sum) pairs, one
+    descriptor per wave, then a 4-int header; each section 256-byte aligned."""
+    ml = _up(2 * waves * G * D * 4)
+    desc = _up(ml + 2 * waves * G * 8)
+    meta = _up(desc + waves * 16)
+    return meta + 16
+
+
 def test_workspace_bytes_and_partitions():
+    F32, BF16 = pa.PA_F32, pa.PA_BF16
     assert pa.pa_decode_partition_tokens(16, 3) == 64
     assert pa.pa_decode_partition_tokens(16, 16) == 256
-    assert pa.pa_decode_workspace_bytes(4, 2, 64, 16, 3) == 0
-    assert pa.pa_decode_workspace_bytes(4, 2, 64, 16, 16) == 0
+    assert pa.pa_decode_partition_tokens(16, 31) == 512
+    assert pa.pa_decode_partition_tokens(16, 64) == 512
+    # fp32 caches take the partition decomposition: no workspace while one partition fits
+    assert pa.pa_decode_workspace_bytes(4, 2, 1, 64, 16, 3, F32) == 0
+    assert pa.pa_decode_workspace_bytes(4, 2, 1, 64, 16, 16, F32) == 0
     P = pa.pa_decode_partition_tokens(16, 256)
     n = -(-16 * 256 // P)
     rows = 64 * 32 * n
     o = rows * 128 * 4
-    assert pa.pa_decode_workspace_bytes(64, 32, 128, 16, 256) == (o + 255) // 256 * 256 + rows * 8
-    pa.pa_set_partition_tokens(512)
+    part = _up(o) + rows * 8
+    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 256, F32) == part
+    # bf16 caches: room for whichever decomposition is chosen
+    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 256, BF16) == max(part, _stream_ws(4, 128))
+    assert pa.pa_decode_workspace_bytes(4, 2, 1, 64, 16, 3, BF16) == _stream_ws(2, 64)
+    # past the stream limits (B > 4096) bf16 falls back to partitions
+    assert pa.pa_decode_workspace_bytes(5000, 8, 8, 64, 16, 3, BF16) == 0
+    assert pa.pa_decode_workspace_bytes(4, 6, 4, 64, 16, 3, BF16) == 0      # Hq % Hkv != 0
+    pa.pa_set_partition_tokens(1024)
     try:
-        assert pa.pa_decode_partition_tokens(16, 256) == 512
-        assert pa.pa_decode_workspace_bytes(64, 32, 128, 16, 256) < (o + 255) // 256 * 256 + rows * 8
+        assert pa.pa_decode_partition_tokens(16, 256) == 1024
+        assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 256, F32) < part
     finally:
         pa.pa_set_partition_tokens(0)
     for bad in (32, 100, 2048, -64):
         with pytest.raises(pa.PaError):
             pa.pa_set_partition_tokens(bad)
-    assert pa.pa_decode_partition_tokens(16, 256) == 256
+    assert pa.pa_decode_partition_tokens(16, 256) == 512
+
+
+def test_decode_path_and_stream_settings():
+    for bad in (-1, 3):
+        with pytest.raises(pa.PaError):
+            pa.pa_set_decode_path(bad)
+    for waves, mins in ((-4, 0), (4097, 0), (8, -1)):
+        with pytest.raises(pa.PaError):
+            pa.pa_set_stream_waves(waves, mins)
+    pa.pa_set_decode_path(pa.PA_PATH_STREAM)
+    try:
+        # the stream decomposition serves bf16 only: forced on fp32 it is refused on the host
+        assert _decode(dt=pa.PA_F32) == pa.PA_ERR_UNSUPPORTED
+        assert _decode(B=5000) == pa.PA_ERR_UNSUPPORTED
+        # bf16: a workspace is always needed
+        assert _decode() == pa.PA_ERR_INVALID_ARG
+        assert "workspace" in pa._lib.pa_last_error().decode()
+    finally:
+        pa.pa_set_decode_path(pa.PA_PATH_AUTO)
+    pa.pa_set_stream_waves(0, 0)
 
 
 def test_cache_write_and_copy_validation():

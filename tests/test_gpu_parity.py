@@ -3,7 +3,12 @@
 Attention: max-abs error over every output element <= 1e-5 (fp32 caches) or 2e-2 (bf16
 caches, fp32 accumulation). Cache write and block copy: bit-exact over the whole cache.
 Invariants (placement, sharing, poison, determinism) are checked bit for bit on the GPU.
+bf16 caches go through the stream decomposition by default; the partition decomposition
+is forced where a test names it, and the stream decomposition is run with few waves where
+rows must be split across many slices.
 """
+import contextlib
+
 import numpy as np
 import pytest
 import torch
@@ -21,7 +26,22 @@ def pa():
         pytest.skip("no GPU")
     from paged_kv_cache_298_amd import pa as _pa
     _pa.pa_set_partition_tokens(0)
+    _pa.pa_set_decode_path(_pa.PA_PATH_AUTO)
+    _pa.pa_set_stream_waves(0, 0)
     return _pa
+
+
+@contextlib.contextmanager
+def _path(pa, path, waves=0, min_slice=0, part_tokens=0):
+    pa.pa_set_decode_path(path)
+    pa.pa_set_stream_waves(waves, min_slice)
+    pa.pa_set_partition_tokens(part_tokens)
+    try:
+        yield
+    finally:
+        pa.pa_set_decode_path(pa.PA_PATH_AUTO)
+        pa.pa_set_stream_waves(0, 0)
+        pa.pa_set_partition_tokens(0)
 
 
 def _parity(pa, oracle, wl, rows=None, tag=""):
@@ -252,11 +272,67 @@ def test_repeated_calls_are_bitwise_equal(pa):
 def test_partition_length_changes_only_rounding(pa, oracle, P):
     wl = W.make_workload("split", 4, 32, 8, 128, 64, [100, 1023, 1025, 4000], W.BF16, seed=P,
                          max_blocks=64)
-    pa.pa_set_partition_tokens(P)
-    try:
-        _parity(pa, oracle, wl, tag=f"P={P}")
-    finally:
-        pa.pa_set_partition_tokens(0)
+    with _path(pa, pa.PA_PATH_PARTITION, part_tokens=P):
+        _parity(pa, oracle, wl, tag=f"partition P={P}")
+
+
+@pytest.mark.parametrize("case", [c for c in SMALL if c[5] == W.BF16],
+                         ids=lambda c: f"G{c[1] // c[2]}-D{c[3]}-bs{c[4]}")
+def test_partition_path_bf16_small_shapes(pa, oracle, case):
+    B, Hq, Hkv, D, bs, dt, lens = case
+    wl = W.make_workload("small", B, Hq, Hkv, D, bs, lens, dt, seed=sum(lens) + D)
+    with _path(pa, pa.PA_PATH_PARTITION):
+        _parity(pa, oracle, wl, tag="partition")
+
+
+def test_partition_path_config2(pa, oracle):
+    with _path(pa, pa.PA_PATH_PARTITION):
+        _parity(pa, oracle, W.config(2), tag="partition")
+
+
+# rows cut across many slices: few waves, one group per slice allowed
+SPLIT = [
+    # B, Hq, Hkv, D, bs, lens, waves
+    (6, 32, 8, 128, 16, [0, 1, 17, 300, 0, 2049], 4),
+    (6, 32, 8, 128, 16, [0, 1, 17, 300, 0, 2049], 12),
+    (5, 16, 2, 64, 32, [4000, 1, 33, 0, 640], 8),
+    (3, 8, 8, 64, 64, [1, 1, 1], 64),             # more waves than groups
+    (4, 8, 1, 128, 16, [1500, 3, 16, 4096], 4),   # slices of ~90 groups: window refresh
+    (2, 64, 8, 128, 16, [2000, 999], 20),         # 8 query heads per KV head
+    (3, 4, 4, 128, 32, [77, 0, 5000], 36),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=lambda c: f"G{c[1] // c[2]}-D{c[3]}-bs{c[4]}-w{c[6]}")
+def test_stream_rows_split_across_slices(pa, oracle, case):
+    B, Hq, Hkv, D, bs, lens, waves = case
+    cap = -(-max(lens) // bs) * bs
+    wl = W.make_workload("split", B, Hq, Hkv, D, bs, lens, W.BF16, seed=sum(lens) + waves,
+                         max_blocks=max(1, cap // bs))
+    with _path(pa, pa.PA_PATH_STREAM, waves=waves, min_slice=1):
+        dw, _, _ = _parity(pa, oracle, wl, tag=f"stream waves={waves}")
+    out = dw.out.cpu().numpy()
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.array_equal(out[b], np.zeros_like(out[b]))
+
+
+def test_stream_config2_few_waves(pa, oracle):
+    with _path(pa, pa.PA_PATH_STREAM, waves=100, min_slice=1):
+        _parity(pa, oracle, W.config(2), tag="stream waves=100")
+
+
+def test_stream_split_invariant_to_placement_and_poison(pa):
+    outs = []
+    for placement, poison in (("permute", True), ("identity", False), ("reversed", True)):
+        wl = W.make_workload("perm", 6, 32, 8, 128, 16, [5, 300, 1024, 17, 2000, 64], W.BF16,
+                             seed=44, placement=placement, poison=poison)
+        note(f"stream split placement {placement} poison {poison}")
+        with _path(pa, pa.PA_PATH_STREAM, waves=12, min_slice=1):
+            o = gpu_step(pa, DevWorkload(wl))
+        assert np.isfinite(o).all()
+        outs.append(o)
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
 
 def test_one_token_returns_its_value_exactly(pa):
