@@ -3,30 +3,30 @@
 // Sources: [P1] "PagedAttention" (inferensys.com glossary): the kernel reads the block
 // table, gathers K/V from scattered physical blocks, handles a partly filled last block
 // and fuses the gather into the attention; [P2] "Paged Attention" tutorial
-// (infra.pidoku.co.in), section 5 "The kernel side": grid over (sequence, head), loop over
-// ceil(ctx / block_size) blocks, phys = table[blk], q.k and a softmax accumulated per
-// block. That page's sketch and its cache layout were written for NVIDIA warps; this
-// file keeps what it computes and lays the work out for 64-lane CDNA4 wavefronts.
+// (infra.pidoku.co.in), section 5 "The kernel side": a loop over a sequence's blocks,
+// phys = table[blk], q.k and an online softmax accumulated per block. That page's sketch
+// and its cache layouts were written for NVIDIA warps; this file keeps what it computes
+// and lays the work out for 64-lane CDNA4 wavefronts.
 //
-// Work decomposition. One wavefront (one 64-thread workgroup) per
-// (partition of P tokens, KV head g, sequence b). All G = Hq / Hkv query heads that read
-// KV head g are served by the same wavefront, so every K/V byte is fetched from HBM once.
-// Sequences longer than P are split; a second kernel combines the partitions exactly.
+// Cache layout [num_blocks, Hkv, block_size, D]: a 16-token group of one KV head is one
+// contiguous 16 x D tile of K and one of V. Every wavefront serves all G = Hq / Hkv query
+// heads of its KV head, so each K/V byte is read from HBM once.
 //
-// Per partition, in three passes over LDS:
-//   1. QK^T on the matrix cores. For each 16-token group the K rows (a contiguous
-//      16 x D tile of the block) are the A operand of v_mfma_f32_16x16x32_bf16 (fp32 data:
-//      v_mfma_f32_16x16x4_f32) and the G query rows, zero-padded to 16, are the B operand.
-//      Each lane feeds its A operand straight from one 16-byte global load of its token's
-//      row; no LDS staging. Scores (scaled, in log2 units) go to LDS; tokens past the
-//      sequence end become -inf by a select, so NaN garbage in unused slots never leaks.
-//   2. Per-head partition max (cross-lane), p = exp2(s - m) in place, per-head sum.
-//   3. PV on the vector ALUs: each wave-wide 16-byte load covers 1 KiB of contiguous V
-//      rows; lanes own 8 (bf16) or 4 (fp32) columns of one row, read that row's G
-//      probabilities from LDS by broadcast, and accumulate G x 8 fp32 partial outputs;
-//      rows are summed across lanes at the end. V rows past the sequence end are zeroed
-//      by a select before use.
-// Block-table entries for the partition are prefetched into LDS once.
+// Kernels:
+//   decode_stream_kernel + stream_reduce_kernel (bf16 caches, the default): the batch's
+//     (sequence, KV head) rows, cut into 16-token groups, are laid end to end and each
+//     resident wavefront takes an equal contiguous slice; one load ring runs across row
+//     boundaries; rows that cross slices leave partial states merged by the second kernel.
+//   decode_bf16_kernel (bf16 fallback) and decode_partition_kernel (fp32): one workgroup
+//     per (KV head, sequence, partition of P tokens); decode_reduce_kernel merges the
+//     partitions.
+// Scores: v_mfma_f32_16x16x32_bf16 (fp32: 16x16x4_f32) with the K tile as the A operand,
+// each lane feeding token (c / 4) + 4 (c % 4) of its row group straight from one 16-byte
+// load, and the G query rows (replicated to 16 columns) as B; lane (r, c) then holds
+// tokens r + 4i of head column c. Softmax: online, in log2 units, masks by select (NaN in
+// unused slots never leaks). PV: the stream kernel feeds those same registers (rounded to
+// bf16) as the A operand of v_mfma_f32_16x16x16_bf16 against V rows gathered with byte
+// permutes; the bf16 partition kernel uses v_mfma_f32_4x4x1_f32, the fp32 one the VALU.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
