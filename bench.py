@@ -124,7 +124,7 @@ def main():
             nv=_to_dev(wl.new_value, torch, dev), slots=_to_dev(wl.slot_mapping, torch, dev),
             pairs=_to_dev(wl.cow_pairs, torch, dev) if wl.cow_pairs.shape[0] else None,
             out=torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev),
-            ws=torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)))
+            ws=torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)))
     stream = torch.cuda.current_stream(dev)
 
     def step(r):

@@ -1282,40 +1282,61 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
 
 // Merge the partial records of rows that cross slice boundaries. Group w looks at the
 // row holding the first group of slice w; it merges it only when that row began inside
-// slice w - 1, so every split row is merged exactly once, records in slice order.
+// slice w - 1, so every split row is merged exactly once, records in slice order. The
+// merge is latency-bound: one thread per float4 of the row's G x D output, the header
+// and the descriptor fetched together, and a row's records loaded kBatch at a time.
 template <int D, int G>
-__global__ __launch_bounds__(256) void stream_reduce_kernel(Params p) {
+__global__ __launch_bounds__(G * D / 4 < 64 ? 64 : G * D / 4) void stream_reduce_kernel(Params p) {
     constexpr int C4 = D / 4;
+    constexpr int kBatch = 8;
     const int w = blockIdx.x;
     const int T = p.meta[0];
     const int nwe = p.meta[1];
-    if (w == 0 || w >= nwe) return;
     const int4 d = p.desc[w];          // b, g, row start, row groups
+    if (w == 0 || w >= nwe) return;
     const int s0w = (int)((int64_t)w * T / nwe);
     if (d.z >= s0w) return;            // the row starts in slice w: not split here
     const int s0p = (int)((int64_t)(w - 1) * T / nwe);
     if (d.z < s0p) return;             // began before slice w - 1: merged by an earlier group
+    const int i = threadIdx.x;
+    if (i >= G * C4) return;
+    const int h = i / C4, c4 = i % C4;
     const int last = d.z + d.w - 1;
     const int wb = (int)(((int64_t)(last + 1) * nwe - 1) / T);   // slice holding the last group
+    const int nrec = wb - w + 2;       // slices w - 1 .. wb
     const int rec_a = 2 * (w - 1) + (d.z == s0p ? 0 : 1);
-    for (int i = threadIdx.x; i < G * C4; i += 256) {
-        const int h = i / C4, c4 = i % C4;
-        float M = p.rec_ml[(int64_t)rec_a * G + h].x;
-        for (int x = w; x <= wb; ++x) M = fmaxf(M, p.rec_ml[(int64_t)(2 * x) * G + h].x);
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        float l = 0.f;
-        for (int x = w - 1; x <= wb; ++x) {
-            const int rec = x == w - 1 ? rec_a : 2 * x;
-            const float2 ml = p.rec_ml[(int64_t)rec * G + h];
-            const float wgt = __builtin_amdgcn_exp2f(ml.x - M);
-            const float4 v = reinterpret_cast<const float4*>(p.rec_o + ((int64_t)rec * G + h) * D)[c4];
-            o.x += wgt * v.x; o.y += wgt * v.y; o.z += wgt * v.z; o.w += wgt * v.w;
-            l += wgt * ml.y;
+    float M = -INFINITY, l = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int x0 = 0; x0 < nrec; x0 += kBatch) {   // running merge in slice order
+        float2 ml[kBatch];
+        float4 v[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int x = x0 + k < nrec ? x0 + k : nrec - 1;
+            const int rec = x == 0 ? rec_a : 2 * (w - 1 + x);
+            ml[k] = p.rec_ml[(int64_t)rec * G + h];
+            v[k] = reinterpret_cast<const float4*>(p.rec_o + ((int64_t)rec * G + h) * D)[c4];
         }
-        const float inv = 1.0f / l;
-        reinterpret_cast<float4*>(p.out + ((int64_t)d.x * p.Hq + d.y * G + h) * D)[c4] =
-            make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+        float Mb = M;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+            if (x0 + k < nrec) Mb = fmaxf(Mb, ml[k].x);
+        const float a = __builtin_amdgcn_exp2f(M - Mb);   // 0 on the first batch
+        o.x *= a; o.y *= a; o.z *= a; o.w *= a;
+        l *= a;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (x0 + k < nrec) {
+                const float wgt = __builtin_amdgcn_exp2f(ml[k].x - Mb);
+                o.x += wgt * v[k].x; o.y += wgt * v[k].y; o.z += wgt * v[k].z; o.w += wgt * v[k].w;
+                l += wgt * ml[k].y;
+            }
+        }
+        M = Mb;
     }
+    const float inv = 1.0f / l;
+    reinterpret_cast<float4*>(p.out + ((int64_t)d.x * p.Hq + d.y * G + h) * D)[c4] =
+        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
 }
 
 template <bool BF16, int D, int G>
@@ -1335,14 +1356,15 @@ hipError_t launch_one(const Params& prm, int B, int Hkv, void* stream) {
     return hipGetLastError();
 }
 
-// Waves of the stream kernel that the device holds at once (cached per device, kernel and
-// LDS size).
-int resident_waves(const void* kern, size_t lds, int* nw) {
+// Launch shape of the stream kernel on the current device: one 4-wave workgroup per CU,
+// so every SIMD runs exactly one wave (two waves sharing a SIMD are served very unevenly:
+// the older one starves the younger, and equal slices then finish far apart). The
+// workgroup reserves just over half of a CU's LDS, which makes that placement certain.
+// Cached per device.
+int stream_shape(size_t need_lds, int* nw, size_t* lds) {
     struct Entry {
-        int dev;
-        const void* kern;
-        size_t lds;
-        int nw;
+        int dev, cus;
+        size_t half;
     };
     static std::mutex mu;
     static Entry cache[16];
@@ -1350,41 +1372,46 @@ int resident_waves(const void* kern, size_t lds, int* nw) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return (int)e;
+    Entry en{-1, 0, 0};
     {
         std::lock_guard<std::mutex> lock(mu);
         for (int i = 0; i < used; ++i)
-            if (cache[i].dev == dev && cache[i].kern == kern && cache[i].lds == lds) {
-                *nw = cache[i].nw;
-                return 0;
-            }
+            if (cache[i].dev == dev) en = cache[i];
     }
-    int cus = 0, nb = 0;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return (int)e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 256, lds);
-    if (e != hipSuccess) return (int)e;
-    if (nb < 1) return (int)hipErrorInvalidConfiguration;
-    *nw = cus * nb * 4;
-    std::lock_guard<std::mutex> lock(mu);
-    if (used < 16) cache[used++] = Entry{dev, kern, lds, *nw};
+    if (en.dev < 0) {
+        int cus = 0, per_cu = 0, per_block = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return (int)e;
+        e = hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+        if (e != hipSuccess) return (int)e;
+        e = hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+        if (e != hipSuccess) return (int)e;
+        size_t half = (size_t)per_cu / 2 + 1024;
+        if (half > (size_t)per_block) half = 0;   // cannot force it: rely on even dispatch
+        en = Entry{dev, cus, half};
+        std::lock_guard<std::mutex> lock(mu);
+        if (used < 16) cache[used++] = en;
+    }
+    *nw = en.cus * 4;
+    *lds = need_lds > en.half ? need_lds : en.half;
     return 0;
 }
 
 template <int D, int G>
 hipError_t launch_stream(Params prm, int nw_req, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const size_t lds = (size_t)(2 * prm.B + 1) * sizeof(int);
-    const void* kern = reinterpret_cast<const void*>(&decode_stream_kernel<D, G, PA_STREAM_DEPTH>);
+    size_t lds = (size_t)(2 * prm.B + 1) * sizeof(int);
     int nw = nw_req;
     if (nw <= 0) {
-        const int e = resident_waves(kern, lds, &nw);
+        const int e = stream_shape(lds, &nw, &lds);
         if (e != 0) return (hipError_t)e;
     }
     nw = nw > pa_internal::kMaxStreamWaves ? pa_internal::kMaxStreamWaves : nw;
     nw = (nw + 3) / 4 * 4;
     prm.nw = nw;
     hipLaunchKernelGGL((decode_stream_kernel<D, G, PA_STREAM_DEPTH>), dim3(nw / 4), dim3(256), lds, s, prm);
-    hipLaunchKernelGGL((stream_reduce_kernel<D, G>), dim3(nw), dim3(256), 0, s, prm);
+    constexpr int kMergeThreads = G * D / 4 < 64 ? 64 : G * D / 4;
+    hipLaunchKernelGGL((stream_reduce_kernel<D, G>), dim3(nw), dim3(kMergeThreads), 0, s, prm);
     return hipGetLastError();
 }
 

@@ -120,14 +120,14 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, workspace
               stream=None):
     """out [B, Hq, D] fp32 <- paged decode attention. k_cache/v_cache are
     [num_blocks, Hkv, block_size, D]; block_tables int32 [B, max_blocks]; seq_lens int32 [B].
-    workspace: a uint8 tensor of at least pa_decode_workspace_bytes(...) bytes (allocated
-    here, on q's device, when None and needed)."""
+    workspace: a uint8 tensor of at least pa_decode_workspace_bytes(...) bytes, zero-filled
+    before its first use (allocated here, zeroed, on q's device, when None and needed)."""
     B, Hq, D = q.shape
     nb, Hkv, bs, _ = k_cache.shape
     max_blocks = block_tables.shape[1]
     need = pa_decode_workspace_bytes(B, Hq, Hkv, D, bs, max_blocks, _kv_dtype(k_cache))
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                           _ptr(seq_lens), B, Hq, Hkv, D, bs, nb, max_blocks, float(scale),

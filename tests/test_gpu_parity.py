@@ -322,6 +322,28 @@ def test_stream_config2_few_waves(pa, oracle):
         _parity(pa, oracle, W.config(2), tag="stream waves=100")
 
 
+def test_stream_workspace_reused_across_calls(pa, oracle):
+    """One workspace serves consecutive calls on different inputs (no stale partial state is
+    read), with few waves so that many rows are merged, then with the default wave count."""
+    from tests._gpu_helpers import to_dev
+    wls = [W.make_workload("reuse", 6, 32, 8, 128, 16, [0, 1, 17, 300, 700, 2049], W.BF16,
+                           seed=100 + i, max_blocks=129) for i in range(3)]
+    ws = torch.empty(pa.pa_decode_workspace_bytes(6, 32, 8, 128, 16, 129, pa.PA_BF16),
+                     dtype=torch.uint8, device=DEV)
+    for waves in (12, 0):
+        with _path(pa, pa.PA_PATH_STREAM, waves=waves, min_slice=1):
+            for wl in wls:
+                note(f"workspace reuse waves={waves} seed={wl.seed if hasattr(wl, 'seed') else ''}")
+                dw = DevWorkload(wl)
+                pa.pa_reshape_and_cache(dw.k, dw.v, dw.nk, dw.nv, dw.slots)
+                pa.pa_decode(dw.out, dw.q, dw.k, dw.v, dw.bt, dw.sl, wl.scale, workspace=ws)
+                torch.cuda.synchronize()
+                ref, _, _ = oracle_step(oracle, wl)
+                err = max_err(dw.out.cpu().numpy(), ref)
+                note(f"  max abs err {err:.3e}")
+                assert err <= TOL[wl.dtype]
+
+
 def test_stream_split_invariant_to_placement_and_poison(pa):
     outs = []
     for placement, poison in (("permute", True), ("identity", False), ("reversed", True)):
