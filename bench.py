@@ -84,6 +84,21 @@ def _cpu_baseline(wl, budget_s):
                       f"repeated {reps}x, {el:.1f} s"}
 
 
+def _copy_calibration(torch, pa, dev, launches=5):
+    """pa_copy_blocks of 2048 distinct blocks onto 2048 others, K and V, bf16, Hkv=8,
+    bs=16, D=128 (32 KiB per block and cache): 128 MiB read and 128 MiB written per launch."""
+    nb, npairs = 4096, 2048
+    k = torch.zeros((nb, 8, 16, 128), dtype=torch.bfloat16, device=dev)
+    v = torch.zeros_like(k)
+    pairs = torch.stack([torch.arange(npairs), torch.arange(npairs) + npairs], 1).to(torch.int32).to(dev)
+    for _ in range(launches):
+        pa.pa_copy_blocks(k, v, pairs)
+    torch.cuda.synchronize()
+    per = 2 * npairs * 8 * 16 * 128 * 2
+    print(json.dumps({"calibration": "pa_copy_blocks", "launches": launches,
+                      "bytes_read_per_launch": per, "bytes_written_per_launch": per}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,6 +108,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run pa_copy_blocks over a known number of bytes (the reference "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and print them")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -106,6 +124,9 @@ def main():
     from paged_kv_cache_298_amd import workloads as W
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        _copy_calibration(torch, pa, dev)
+        return
     _log(f"generating workload {args.config}")
     wl = W.config(args.config, poison=False)
     kv_bytes = wl.kv_bytes()
@@ -207,7 +228,7 @@ def main():
         "config": {"workload": W.CONFIG_NAMES[args.config], "global_batch": wl.B,
                    "kv_bytes_per_step": kv_bytes, "replicas_rotated": R,
                    "step": "copy_blocks (if CoW pairs) + reshape_and_cache + pa_decode"},
-        "roofline": {"bound": "hbm", "kernel": "pa_decode (partition + reduce launches)",
+        "roofline": {"bound": "hbm", "kernel": "pa_decode (decode kernel + split-row merge)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "decode_us_mean": round(dec_mean, 2),
