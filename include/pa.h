@@ -76,8 +76,8 @@ extern "C" {
  *   workspace     device scratch of at least pa_decode_workspace_bytes(...) bytes, 256-byte
  *                 aligned (may be NULL when that size is 0); it holds partial softmax
  *                 states of sequences split across work items and needs no initialisation
- * Supported: D in {64, 128}; block_size in {16, 32, 64}; G in {1, 2, 4, 8}; others return
- * PA_ERR_UNSUPPORTED. The result is deterministic: repeated calls on one device give
+ * Supported: D in {64, 128}; block_size in {8, 16, 32, 64, 128} (8 with bf16 caches and
+ * the stream decomposition only); G in {1, 2, 4, 8}; others return PA_ERR_UNSUPPORTED. The result is deterministic: repeated calls on one device give
  * identical bits, whatever the physical placement of the blocks.
  *
  * Work decomposition (chosen per call, see pa_set_decode_path):

@@ -91,9 +91,12 @@ StreamWs stream_workspace(int32_t G, int32_t D) {
     return w;
 }
 
+// Blocks of 8 tokens (a 16-token group spans two blocks) are served by the stream
+// decomposition only; 0 = no decomposition applies.
 int32_t choose_path(int32_t kv_dtype, int32_t B, int32_t Hkv, int32_t block_size, int32_t max_blocks) {
-    if (g_path == PA_PATH_PARTITION) return pa_internal::kPathPartition;
     const bool ok = stream_eligible(kv_dtype, B, Hkv, block_size, max_blocks);
+    if (block_size < 16) return (ok && g_path != PA_PATH_PARTITION) ? pa_internal::kPathStream : 0;
+    if (g_path == PA_PATH_PARTITION) return pa_internal::kPathPartition;
     if (g_path == PA_PATH_STREAM) return ok ? pa_internal::kPathStream : 0;
     return ok ? pa_internal::kPathStream : pa_internal::kPathPartition;
 }
@@ -177,8 +180,8 @@ int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_
     const int32_t G = Hq / Hkv;
     if (D != 64 && D != 128)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d not built (64, 128)", D);
-    if (block_size != 16 && block_size != 32 && block_size != 64)
-        return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d not built (16, 32, 64)", block_size);
+    if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d not built (8, 16, 32, 64, 128)", block_size);
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode: %d query heads per KV head not built (1, 2, 4, 8)", G);
     if (Hkv > 65535)
@@ -193,10 +196,11 @@ int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_
         return fail(PA_ERR_INVALID_ARG, "pa_decode: cache size overflows");
     const int32_t path = choose_path(kv_dtype, B, Hkv, block_size, max_blocks);
     if (path == 0)
-        return fail(PA_ERR_UNSUPPORTED, "pa_decode: the stream path needs bf16 caches, B <= %d and "
-                    "fewer than 2^31 token groups", pa_internal::kMaxStreamB);
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: the stream decomposition (the only one for "
+                    "block_size 8) needs bf16 caches, B <= %d and fewer than 2^31 token groups",
+                    pa_internal::kMaxStreamB);
     const int32_t P = partition_tokens(block_size, max_blocks);
-    if (P % block_size != 0)
+    if (path == pa_internal::kPathPartition && P % block_size != 0)
         return fail(PA_ERR_INVALID_ARG, "pa_decode: partition %d not a multiple of block_size %d", P, block_size);
     const int32_t n_parts = n_parts_for(block_size, max_blocks);
     size_t ml_off = 0;

@@ -878,7 +878,9 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
 // is updated once per group. Block-table lookups for 64 groups at a time ("window") are
 // resolved lane-parallel: lane i finds the row of group sw + i by a binary search over
 // the per-sequence prefix of group counts kept in LDS, then gathers its table entry.
-template <int D, int G, int DEPTH>
+// SPLIT: blocks of 8 tokens, so a 16-token group spans two physical blocks; each group
+// then has two tile offsets (tokens 0-7 and 8-15) and K lanes / V loads pick theirs.
+template <int D, int G, int DEPTH, bool SPLIT>
 __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
     constexpr int ROW = D * 2;              // bytes per cached row
     constexpr int NQ = D / 32;              // 16-byte registers per ring item
@@ -959,6 +961,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
 
     // ---- window: lane i describes group sw + i of the slice (clamped into it)
     uint32_t w_lo = 0, w_hi = 0;   // byte offset of the group's tile in either cache
+    uint32_t w_lo1 = 0, w_hi1 = 0; // SPLIT: offset of the tile holding tokens 8-15
     int w_row = 0, w_j = 0;        // its row (b * Hkv + g) and group within the row
     int sw = s0;
     auto window = [&](int base) {
@@ -974,12 +977,22 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
         const int off = s - Cs[lo] * p.Hkv;
         const int g = off / n;
         const int j = off - g * n;
-        int e = p.tables[(int64_t)lo * p.max_blocks + ((j << 4) >> p.bs_shift)];
+        const int32_t* trow = p.tables + (int64_t)lo * p.max_blocks;
+        int e = trow[(j << 4) >> p.bs_shift];
         e = e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);
         const int64_t o = (int64_t)e * blk_bytes + (int64_t)g * tile_bytes +
                           (int64_t)((j << 4) & bs_mask) * ROW;
         w_lo = (uint32_t)o;
         w_hi = (uint32_t)((uint64_t)o >> 32);
+        if constexpr (SPLIT) {     // the second block of the group (clamped into the row)
+            int i1 = 2 * j + 1;
+            i1 = i1 < p.max_blocks ? i1 : p.max_blocks - 1;
+            int e1 = trow[i1];
+            e1 = e1 < 0 ? 0 : (e1 >= p.num_blocks ? p.num_blocks - 1 : e1);
+            const int64_t o1 = (int64_t)e1 * blk_bytes + (int64_t)g * tile_bytes;
+            w_lo1 = (uint32_t)o1;
+            w_hi1 = (uint32_t)((uint64_t)o1 >> 32);
+        }
         w_row = lo * p.Hkv + g;
         w_j = j;
     };
@@ -1026,7 +1039,11 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
     int qn_row = -1;       // row whose fragments sit in qn
     int iss_row = row0;    // row of the last K tile issued
 
-    const uint32_t koff = (uint32_t)(((c >> 2) + 4 * (c & 3)) * ROW + r * 16);
+    // K: lane c of a row group feeds token (c / 4) + 4 (c % 4) of the group; with SPLIT,
+    // tokens 8-15 (c % 4 >= 2) come from the second block, at row token - 8
+    const int ktok = (c >> 2) + 4 * (c & 3);
+    const bool khi = SPLIT && ktok >= 8;
+    const uint32_t koff = (uint32_t)((SPLIT ? (ktok & 7) : ktok) * ROW + r * 16);
     const uint32_t voff = (uint32_t)(r * ROW + c * WV);
     struct Item {
         u32x4_t q[NQ];
@@ -1042,6 +1059,14 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
         return ((uint64_t)__builtin_amdgcn_readlane(w_hi, idx) << 32) |
                (uint64_t)__builtin_amdgcn_readlane(w_lo, idx);
     };
+    // SPLIT: the second block's tile of the same group (the window is already in place)
+    auto tile_off1 = [&](int gq) -> uint64_t {
+        int s = s0 + gq;
+        s = s < s1 ? s : s1 - 1;
+        const int idx = s - sw;
+        return ((uint64_t)__builtin_amdgcn_readlane(w_hi1, idx) << 32) |
+               (uint64_t)__builtin_amdgcn_readlane(w_lo1, idx);
+    };
     auto issue_k = [&](int gq, Item& dst) {
         const uint64_t off = tile_off(gq);
         int s = s0 + gq;
@@ -1053,21 +1078,33 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
             load_q(row, qn);
         }
         const char* kb = p.k + off;
+        if constexpr (SPLIT) {
+            const char* kb1 = p.k + tile_off1(gq);
+            kb = khi ? kb1 : kb;
+        }
 #pragma unroll
         for (int k = 0; k < NQ; ++k)
             dst.q[k] = *reinterpret_cast<const u32x4_t*>(kb + koff + k * 64);
     };
+    // V load k holds rows r + 4k; with SPLIT, loads 2 and 3 (rows 8-15) read the second
+    // block at rows r + 4 (k - 2)
     auto issue_v = [&](int gq, Item& dst) {
         const char* vb = p.v + tile_off(gq);
+        const char* vb1 = vb + 2 * 4 * ROW;
+        if constexpr (SPLIT) vb1 = p.v + tile_off1(gq);
+        // address of V load k (rows r + 4k of the group)
+        auto vaddr = [&](int k) -> const char* {
+            return k < 2 ? vb + voff + k * 4 * ROW : vb1 + voff + (k - 2) * 4 * ROW;
+        };
         if constexpr (WV == 16) {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                dst.q[k] = *reinterpret_cast<const u32x4_t*>(vb + voff + k * 4 * ROW);
+                dst.q[k] = *reinterpret_cast<const u32x4_t*>(vaddr(k));
         } else {
 #pragma unroll
             for (int k = 0; k < 4; k += 2) {
-                const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vb + voff + k * 4 * ROW);
-                const u32x2_t e = *reinterpret_cast<const u32x2_t*>(vb + voff + (k + 1) * 4 * ROW);
+                const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vaddr(k));
+                const u32x2_t e = *reinterpret_cast<const u32x2_t*>(vaddr(k + 1));
                 dst.q[k / 2] = __builtin_shufflevector(a, e, 0, 1, 2, 3);
             }
         }
@@ -1397,7 +1434,7 @@ int stream_shape(size_t need_lds, int* nw, size_t* lds) {
     return 0;
 }
 
-template <int D, int G>
+template <int D, int G, bool SPLIT>
 hipError_t launch_stream(Params prm, int nw_req, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     size_t lds = (size_t)(2 * prm.B + 1) * sizeof(int);
@@ -1409,19 +1446,19 @@ hipError_t launch_stream(Params prm, int nw_req, void* stream) {
     nw = nw > pa_internal::kMaxStreamWaves ? pa_internal::kMaxStreamWaves : nw;
     nw = (nw + 3) / 4 * 4;
     prm.nw = nw;
-    hipLaunchKernelGGL((decode_stream_kernel<D, G, PA_STREAM_DEPTH>), dim3(nw / 4), dim3(256), lds, s, prm);
+    hipLaunchKernelGGL((decode_stream_kernel<D, G, PA_STREAM_DEPTH, SPLIT>), dim3(nw / 4), dim3(256), lds, s, prm);
     constexpr int kMergeThreads = G * D / 4 < 64 ? 64 : G * D / 4;
     hipLaunchKernelGGL((stream_reduce_kernel<D, G>), dim3(nw), dim3(kMergeThreads), 0, s, prm);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool SPLIT>
 hipError_t dispatch_stream_g(const Params& prm, int G, int nw, void* stream) {
     switch (G) {
-        case 1: return launch_stream<D, 1>(prm, nw, stream);
-        case 2: return launch_stream<D, 2>(prm, nw, stream);
-        case 4: return launch_stream<D, 4>(prm, nw, stream);
-        case 8: return launch_stream<D, 8>(prm, nw, stream);
+        case 1: return launch_stream<D, 1, SPLIT>(prm, nw, stream);
+        case 2: return launch_stream<D, 2, SPLIT>(prm, nw, stream);
+        case 4: return launch_stream<D, 4, SPLIT>(prm, nw, stream);
+        case 8: return launch_stream<D, 8, SPLIT>(prm, nw, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1481,8 +1518,11 @@ int launch_decode(const DecodeLaunch& a, const char** err) {
     const int G = a.Hq / a.Hkv;
     hipError_t e;
     if (a.path == kPathStream) {
-        e = a.D == 64 ? dispatch_stream_g<64>(prm, G, a.stream_waves, a.stream)
-          : a.D == 128 ? dispatch_stream_g<128>(prm, G, a.stream_waves, a.stream)
+        const bool split = a.bs < 16;
+        e = a.D == 64 ? (split ? dispatch_stream_g<64, true>(prm, G, a.stream_waves, a.stream)
+                               : dispatch_stream_g<64, false>(prm, G, a.stream_waves, a.stream))
+          : a.D == 128 ? (split ? dispatch_stream_g<128, true>(prm, G, a.stream_waves, a.stream)
+                                : dispatch_stream_g<128, false>(prm, G, a.stream_waves, a.stream))
                        : hipErrorInvalidValue;
     } else {
         e = a.kv_dtype == 1 ? dispatch_d<true>(prm, a.B, a.Hkv, a.D, G, a.stream)

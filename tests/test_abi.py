@@ -53,7 +53,10 @@ def _decode(**kw):
     (dict(Hq=6, Hkv=4), pa.PA_ERR_INVALID_ARG),
     (dict(dt=7), pa.PA_ERR_INVALID_ARG),
     (dict(D=96), pa.PA_ERR_UNSUPPORTED),
-    (dict(bs=8), pa.PA_ERR_UNSUPPORTED),
+    (dict(bs=12), pa.PA_ERR_UNSUPPORTED),
+    (dict(bs=256), pa.PA_ERR_UNSUPPORTED),
+    (dict(bs=8, dt=pa.PA_F32), pa.PA_ERR_UNSUPPORTED),   # 8-token blocks: bf16 stream only
+    (dict(bs=8, B=5000), pa.PA_ERR_UNSUPPORTED),
     (dict(Hq=6, Hkv=2), pa.PA_ERR_UNSUPPORTED),
     (dict(Hq=32, Hkv=2), pa.PA_ERR_UNSUPPORTED),
     (dict(q=ctypes.c_void_p(0x100008)), pa.PA_ERR_INVALID_ARG),
@@ -130,6 +133,15 @@ def test_decode_path_and_stream_settings():
         # the stream decomposition serves bf16 only: forced on fp32 it is refused on the host
         assert _decode(dt=pa.PA_F32) == pa.PA_ERR_UNSUPPORTED
         assert _decode(B=5000) == pa.PA_ERR_UNSUPPORTED
+    finally:
+        pa.pa_set_decode_path(pa.PA_PATH_AUTO)
+    pa.pa_set_decode_path(pa.PA_PATH_PARTITION)
+    try:
+        assert _decode(bs=8) == pa.PA_ERR_UNSUPPORTED        # no partition kernel for 8-token blocks
+    finally:
+        pa.pa_set_decode_path(pa.PA_PATH_AUTO)
+    pa.pa_set_decode_path(pa.PA_PATH_STREAM)
+    try:
         # bf16: a workspace is always needed
         assert _decode() == pa.PA_ERR_INVALID_ARG
         assert "workspace" in pa._lib.pa_last_error().decode()

@@ -77,6 +77,14 @@ SMALL = [
     (3, 8, 1, 64, 32, W.F32, [5, 64, 333]),
     (2, 2, 2, 128, 64, W.F32, [70, 1]),
     (4, 4, 4, 64, 16, W.F32, [16, 17, 255, 1024]),
+    # 8-token blocks (a 16-token group spans two blocks; bf16 stream decomposition only)
+    (4, 16, 4, 128, 8, W.BF16, [7, 8, 9, 300]),
+    (3, 8, 8, 64, 8, W.BF16, [1, 17, 1001]),
+    (2, 64, 8, 128, 8, W.BF16, [15, 2000]),
+    # 128-token blocks
+    (3, 16, 4, 64, 128, W.BF16, [1, 128, 1000]),
+    (3, 32, 8, 128, 128, W.BF16, [127, 129, 4000]),
+    (3, 16, 4, 64, 128, W.F32, [100, 129, 700]),
 ]
 
 
@@ -276,7 +284,7 @@ def test_partition_length_changes_only_rounding(pa, oracle, P):
         _parity(pa, oracle, wl, tag=f"partition P={P}")
 
 
-@pytest.mark.parametrize("case", [c for c in SMALL if c[5] == W.BF16],
+@pytest.mark.parametrize("case", [c for c in SMALL if c[5] == W.BF16 and c[4] >= 16],
                          ids=lambda c: f"G{c[1] // c[2]}-D{c[3]}-bs{c[4]}")
 def test_partition_path_bf16_small_shapes(pa, oracle, case):
     B, Hq, Hkv, D, bs, dt, lens = case
@@ -300,6 +308,8 @@ SPLIT = [
     (4, 8, 1, 128, 16, [1500, 3, 16, 4096], 4),   # slices of ~90 groups: window refresh
     (2, 64, 8, 128, 16, [2000, 999], 20),         # 8 query heads per KV head
     (3, 4, 4, 128, 32, [77, 0, 5000], 36),
+    (4, 32, 8, 128, 8, [1, 9, 300, 2049], 12),    # 8-token blocks
+    (3, 16, 2, 64, 128, [700, 0, 3000], 8),       # 128-token blocks
 ]
 
 
@@ -354,6 +364,17 @@ def test_stream_split_invariant_to_placement_and_poison(pa):
             o = gpu_step(pa, DevWorkload(wl))
         assert np.isfinite(o).all()
         outs.append(o)
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("bs", [8, 128])
+def test_placement_invariance_new_block_sizes(pa, bs):
+    outs = []
+    for placement in ("permute", "identity", "reversed"):
+        wl = W.make_workload("perm", 5, 32, 8, 128, bs, [5, 300, 1024, 17, 2000], W.BF16,
+                             seed=45, placement=placement)
+        note(f"placement {placement} bs={bs}")
+        outs.append(gpu_step(pa, DevWorkload(wl)))
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
 
