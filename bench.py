@@ -99,6 +99,48 @@ def _copy_calibration(torch, pa, dev, launches=5):
                       "bytes_read_per_launch": per, "bytes_written_per_launch": per}), flush=True)
 
 
+def _sweep_block_size(torch, pa, W, dev, args):
+    """The same 64 sequences (lengths of the Llama-3-8B batch) stored in blocks of
+    8, 16, 32, 64 and 128 tokens, with the physical blocks permuted at random or laid out
+    in order; each point times pa_decode alone (HIP events around each call, two replicas
+    rotated) and prints one JSON line."""
+    L = W.config(2, poison=False).seq_lens
+    steps = max(20, min(args.steps, 100))
+    for bs in (8, 16, 32, 64, 128):
+        for placement in ("permute", "identity"):
+            wl = W.make_workload(f"llama3-8b-bs{bs}", 64, 32, 8, 128, bs, L, W.BF16, 29802,
+                                 max_blocks=4096 // bs, poison=False, placement=placement)
+            ws_bytes = pa.pa_decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, bs,
+                                                    wl.max_blocks, pa.PA_BF16)
+            reps = [dict(q=_to_dev(wl.q, torch, dev), k=_to_dev(wl.k_cache, torch, dev),
+                         v=_to_dev(wl.v_cache, torch, dev), bt=_to_dev(wl.block_tables, torch, dev),
+                         sl=_to_dev(wl.seq_lens, torch, dev),
+                         out=torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev))
+                    for _ in range(2)]
+            ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+            stream = torch.cuda.current_stream(dev)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for i in range(10 + steps):
+                r = reps[i % 2]
+                if i >= 10:
+                    ev[i - 10][0].record(stream)
+                pa.pa_decode(r["out"], r["q"], r["k"], r["v"], r["bt"], r["sl"], wl.scale,
+                             workspace=ws, stream=stream)
+                if i >= 10:
+                    ev[i - 10][1].record(stream)
+            torch.cuda.synchronize()
+            us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+            print(json.dumps({"sweep": "block_size", "block_size": bs, "placement": placement,
+                              "decode_us_mean": round(float(us.mean()), 2),
+                              "decode_us_p50": round(float(np.median(us)), 2),
+                              "kv_bytes": wl.kv_bytes(),
+                              "GBps": round(wl.kv_bytes() / (us.mean() * 1e-6) / 1e9, 1),
+                              "table_entries": int(sum((x + bs - 1) // bs for x in L))}), flush=True)
+            del reps, ws
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +150,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GiB")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-block-size", action="store_true",
+                    help="pa_decode on the Llama-3-8B-shaped batch for block sizes 8..128, "
+                         "permuted vs in-order block placement; one JSON line per point")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run pa_copy_blocks over a known number of bytes (the reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and print them")
@@ -126,6 +171,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         _copy_calibration(torch, pa, dev)
+        return
+    if args.sweep_block_size:
+        _sweep_block_size(torch, pa, W, dev, args)
         return
     _log(f"generating workload {args.config}")
     wl = W.config(args.config, poison=False)
