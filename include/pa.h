@@ -131,6 +131,40 @@ int32_t pa_set_decode_path(int32_t path);
  */
 int32_t pa_set_stream_waves(int32_t waves, int32_t min_slice);
 
+/*
+ * pa_decode_shared -- pa_decode for a batch in which groups of consecutive sequences
+ * share their leading blocks (shared prompts and parallel sampling: [P1] "Shared Prompts"
+ * and "Parallel Sampling"; [P2] section 5 "Copy-on-write sharing"). Every shared K/V tile
+ * is read from HBM once for all members of its group instead of once per member; the
+ * result equals pa_decode's up to rounding.
+ *
+ *   groups             device int32 [n_groups, 3]: first sequence, members, shared tokens.
+ *                      Members are sequences first .. first + members - 1; groups are
+ *                      sorted by first sequence and disjoint. For every member, the table
+ *                      entries covering the shared tokens equal the first member's, and
+ *                      seq_lens >= shared tokens. Shared tokens are used rounded down to a
+ *                      multiple of 16 (the tokens past that are read per member).
+ *   n_groups           host count of groups (0: every sequence is read on its own)
+ *   max_members        host bound on the members of any group; max_members * Hq / Hkv
+ *                      must not exceed 64
+ *   max_shared_tokens  host bound on any group's shared tokens (<= max_blocks * block_size)
+ *   workspace          at least pa_decode_shared_workspace_bytes(...) bytes, 256-byte
+ *                      aligned; needs no initialisation
+ * bf16 caches, block_size in {16, 32, 64, 128}; every other argument as for pa_decode.
+ * Violated group preconditions give wrong rows for the sequences concerned, never an
+ * access outside the buffers.
+ */
+int32_t pa_decode_shared(float* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens,
+                         const int32_t* groups, int32_t n_groups, int32_t max_members,
+                         int32_t max_shared_tokens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                         int32_t block_size, int32_t num_blocks, int32_t max_blocks, float scale,
+                         int32_t kv_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pa_decode_shared needs (0 for sizes it would reject). */
+size_t pa_decode_shared_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t block_size,
+                                        int32_t max_blocks, int32_t max_shared_tokens);
+
 /* ------------------------------------------------------------------ cache write */
 
 /*

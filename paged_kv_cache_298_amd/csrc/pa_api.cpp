@@ -254,6 +254,121 @@ int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_
     return ok();
 }
 
+namespace {
+
+struct SharedWs {
+    int32_t n_pre, n_suf, n_slots, P;
+    size_t ml, total;
+};
+
+SharedWs shared_workspace(int32_t B, int32_t Hq, int32_t D, int32_t block_size, int32_t max_blocks,
+                          int32_t max_shared_tokens) {
+    SharedWs w;
+    w.P = partition_tokens(block_size, max_blocks);
+    const int64_t cap = (int64_t)block_size * max_blocks;
+    w.n_pre = (int32_t)((max_shared_tokens + pa_internal::kPrefixTokens - 1) / pa_internal::kPrefixTokens);
+    w.n_suf = (int32_t)((cap + w.P - 1) / w.P);
+    w.n_slots = w.n_pre + w.n_suf;
+    const size_t rows = (size_t)B * (size_t)Hq * (size_t)w.n_slots;
+    w.ml = (rows * (size_t)D * sizeof(float) + 255) / 256 * 256;
+    w.total = w.ml + rows * 2 * sizeof(float);
+    return w;
+}
+
+}  // namespace
+
+size_t pa_decode_shared_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t block_size,
+                                        int32_t max_blocks, int32_t max_shared_tokens) {
+    if (B <= 0 || Hq <= 0 || D <= 0 || block_size <= 0 || max_blocks <= 0 || max_shared_tokens < 0)
+        return 0;
+    return shared_workspace(B, Hq, D, block_size, max_blocks, max_shared_tokens).total;
+}
+
+int32_t pa_decode_shared(float* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens,
+                         const int32_t* groups, int32_t n_groups, int32_t max_members,
+                         int32_t max_shared_tokens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                         int32_t block_size, int32_t num_blocks, int32_t max_blocks, float scale,
+                         int32_t kv_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0 ||
+        max_blocks <= 0 || n_groups < 0 || max_shared_tokens < 0)
+        return fail(PA_ERR_INVALID_ARG,
+                    "pa_decode_shared: bad sizes B=%d Hq=%d Hkv=%d D=%d block_size=%d num_blocks=%d "
+                    "max_blocks=%d n_groups=%d max_shared_tokens=%d",
+                    B, Hq, Hkv, D, block_size, num_blocks, max_blocks, n_groups, max_shared_tokens);
+    if (Hq % Hkv != 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_shared: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (elt_bytes(kv_dtype) == 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_shared: kv_dtype %d is neither PA_F32 nor PA_BF16", kv_dtype);
+    if (kv_dtype != PA_BF16)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared: only bf16 caches are built");
+    if ((int64_t)block_size * max_blocks > (int64_t)1 << 30)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_shared: max_blocks * block_size exceeds 2^30");
+    if (max_shared_tokens > block_size * max_blocks)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_shared: max_shared_tokens %d exceeds the table capacity",
+                    max_shared_tokens);
+    if (B > 65535 || Hkv > 65535)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared: B=%d or Hkv=%d exceeds 65535", B, Hkv);
+    const int32_t G = Hq / Hkv;
+    if (D != 64 && D != 128)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared: head_dim %d not built (64, 128)", D);
+    if (block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared: block_size %d not built (16, 32, 64, 128)", block_size);
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared: %d query heads per KV head not built (1, 2, 4, 8)", G);
+    if (n_groups > 0 && (max_members < 1 || (int64_t)max_members * G > pa_internal::kMaxSharedRows))
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared: max_members %d x %d query heads per KV head "
+                    "must lie in [1, %d]", max_members, G, pa_internal::kMaxSharedRows);
+    if (B == 0) return ok();
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || (n_groups > 0 && !groups))
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_shared: null pointer argument");
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(seq_lens, 4) || (groups && !aligned(groups, 4)))
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_shared: misaligned pointer");
+    const SharedWs sw = shared_workspace(B, Hq, D, block_size, max_blocks, max_shared_tokens);
+    if (sw.P % block_size != 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_shared: partition %d not a multiple of block_size %d", sw.P, block_size);
+    if (!workspace || workspace_bytes < sw.total)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_shared: workspace of %zu bytes needed, %zu given",
+                    sw.total, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256))
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_shared: workspace must be 256-byte aligned");
+    if ((int64_t)n_groups * Hkv * sw.n_pre > 0x7fffffff || (int64_t)sw.n_suf * Hkv * B > 0x7fffffff)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared: work items exceed the grid limit");
+
+    pa_internal::SharedLaunch a;
+    a.out = out;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + sw.ml);
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.tables = block_tables;
+    a.lens = seq_lens;
+    a.groups = n_groups > 0 ? groups : nullptr;
+    a.n_groups = n_groups;
+    a.max_members = n_groups > 0 ? max_members : 1;
+    a.max_shared = max_shared_tokens;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.bs = block_size;
+    a.num_blocks = num_blocks;
+    a.max_blocks = max_blocks;
+    a.pre_tokens = pa_internal::kPrefixTokens;
+    a.part_tokens = sw.P;
+    a.n_pre = n_groups > 0 ? sw.n_pre : 0;
+    a.n_suf = sw.n_suf;
+    a.n_slots = sw.n_slots;
+    a.scale = scale;
+    a.stream = stream;
+    const char* err = "";
+    const int e = pa_internal::launch_decode_shared(a, &err);
+    if (e != 0) return fail(PA_ERR_HIP, "pa_decode_shared: launch failed: %s (%d)", err, e);
+    return ok();
+}
+
 int32_t pa_reshape_and_cache(void* k_cache, void* v_cache, const void* key, const void* value,
                              const int32_t* slot_mapping, int32_t T, int32_t Hkv, int32_t D,
                              int32_t block_size, int32_t num_blocks, int32_t kv_dtype,

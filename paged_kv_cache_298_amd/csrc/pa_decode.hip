@@ -89,7 +89,37 @@ struct Params {
     int* meta;        // [2] groups in the stream, waves given a slice
     int nw;           // waves launched
     int min_slice;    // fewest 16-token groups per wave
+    // shared-prefix decomposition only (groups == nullptr otherwise)
+    const int32_t* groups;   // [n_groups, 3]: first sequence, members, shared tokens; sorted
+    int n_groups;
+    int pre_tokens;          // tokens per prefix partition
+    int max_members;         // host bounds the device groups are clamped to (they size the
+    int max_shared;          // workspace and the query tiles)
 };
+
+// Shared-prefix mode: the group holding sequence b (groups are sorted by first sequence
+// and disjoint), or -1; *start = the tokens b shares with its group (0 when none), clamped
+// into [0, L].
+__device__ __forceinline__ int find_group(const Params& p, int b, int L, int* start) {
+    int lo = 0, hi = p.n_groups - 1, found = -1;
+    while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        if (p.groups[3 * mid] <= b) {
+            found = mid;
+            lo = mid + 1;
+        } else {
+            hi = mid - 1;
+        }
+    }
+    *start = 0;
+    if (found >= 0 && b < p.groups[3 * found] + p.groups[3 * found + 1]) {
+        int sh = p.groups[3 * found + 2];
+        sh = (sh > p.max_shared ? p.max_shared : sh) & ~15;   // whole 16-token groups only
+        *start = sh < 0 ? 0 : (sh > L ? L : sh);
+        return found;
+    }
+    return -1;
+}
 
 __device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -479,7 +509,15 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(Params p) {
     int L = p.lens[b];
     L = L < 0 ? 0 : (L > cap ? cap : L);
     const int hq0 = g * G;
-    const int t0 = part * p.part_tokens;
+    // shared-prefix mode: this kernel covers only the tokens after the shared prefix and
+    // always leaves partial records (slots after the prefix partitions)
+    const bool shared = p.groups != nullptr;
+    int start = 0, slot0 = 0;
+    if (shared) {
+        find_group(p, b, L, &start);
+        slot0 = (start + p.pre_tokens - 1) / p.pre_tokens;
+    }
+    const int t0 = start + part * p.part_tokens;
     // Wave wid takes the partition's 16-token groups wid, wid + W, wid + 2W, ... (its
     // "local" groups 0, 1, 2, ...). The block-table entries of those groups are fetched
     // before the sequence length is known (they do not depend on it): lane i holds the
@@ -494,7 +532,7 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(Params p) {
         tblv = e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);
     }
     if (t0 >= L) {
-        if (part == 0) {   // empty sequence: a zero row per head
+        if (part == 0 && !shared) {   // empty sequence: a zero row per head
             for (int i = threadIdx.x; i < G * D; i += 64 * W)
                 p.out[((int64_t)b * p.Hq + hq0) * D + i] = 0.f;
         }
@@ -508,7 +546,8 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(Params p) {
     const int last = ngroups - 1;
     const int ntok = ngroups > 0 ? last * 16 + min(16, ntok_part - (wid + last * W) * 16) : 0;
     const int nchunks = (ngroups + kChunk - 1) / kChunk;
-    const int nparts_b = (L + p.part_tokens - 1) / p.part_tokens;
+    const int nparts_b = shared ? 0 : (L + p.part_tokens - 1) / p.part_tokens;   // 0: records
+    const int slot = slot0 + part;
 
     const int r = lane >> 4;     // row group
     const int c = lane & 15;     // column
@@ -743,12 +782,12 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(Params p) {
                             *reinterpret_cast<float4*>(dst + e) =
                                 make_float4(o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv);
                     } else {
-                        float* dst = p.ws_o + (((int64_t)b * p.Hq + hq0 + h) * p.n_parts + part) * D + c * EV;
+                        float* dst = p.ws_o + (((int64_t)b * p.Hq + hq0 + h) * p.n_parts + slot) * D + c * EV;
 #pragma unroll
                         for (int e = 0; e < EV; e += 4)
                             *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
                         if (c == 0)
-                            p.ws_ml[((int64_t)b * p.Hq + hq0 + h) * p.n_parts + part] =
+                            p.ws_ml[((int64_t)b * p.Hq + hq0 + h) * p.n_parts + slot] =
                                 make_float2(mh[s][m], lh[s][m]);
                     }
                 }
@@ -796,8 +835,251 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(Params p) {
                 reinterpret_cast<float4*>(p.out + row * D)[c4] =
                     make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
             } else {
-                reinterpret_cast<float4*>(p.ws_o + (row * p.n_parts + part) * D)[c4] = o;
-                if (c4 == 0) p.ws_ml[row * p.n_parts + part] = make_float2(M, ls);
+                reinterpret_cast<float4*>(p.ws_o + (row * p.n_parts + slot) * D)[c4] = o;
+                if (c4 == 0) p.ws_ml[row * p.n_parts + slot] = make_float2(M, ls);
+            }
+        }
+    }
+}
+
+
+// Shared prefix (parallel sampling, shared prompts): the leading tokens a group of
+// sequences shares are read once for all of them. One wavefront per (group, KV head,
+// partition of pre_tokens tokens); the M = members x G query rows of the group are the
+// columns of the score tiles (set s holds rows 16 s .. 16 s + 15, zero past M), so each K
+// and V tile feeds every member. Scores: v_mfma_f32_16x16x32_bf16, lane (r, c) then holds
+// tokens r + 4i of query row 16 s + c; online softmax per column; PV:
+// v_mfma_f32_16x16x16_bf16 with those probabilities (rounded to bf16) as A, leaving lane
+// (r, c) with query rows 16 s + 4 r + i of output columns c * EV .. c * EV + EV - 1. Every
+// (member, head) gets a partial record in slot `part`; the partition merge combines them
+// with the members' own tokens.
+template <int D, int NSET>
+__global__ __launch_bounds__(64) void decode_prefix_kernel(Params p) {
+    constexpr int ROW = D * 2;
+    constexpr int NQ = D / 32;
+    constexpr int WV = D / 8;
+    constexpr int EV = D / 16;
+    constexpr int DEPTH = 4;             // ring items: K and V of two groups
+    constexpr int U = DEPTH / 2;
+    static_assert(D == 64 || D == 128, "head size");
+
+    const int lane = threadIdx.x;
+    const int id = blockIdx.x;
+    const int g = id % p.Hkv;
+    const int rest = id / p.Hkv;
+    const int gi_ = rest % p.n_groups;
+    const int part = rest / p.n_groups;
+    const int first = p.groups[3 * gi_];
+    int members = p.groups[3 * gi_ + 1];
+    members = members > p.max_members ? p.max_members : members;
+    members = members > p.B - first ? p.B - first : members;   // stay inside the batch
+    const int cap = p.max_blocks * p.bs;
+    int shared_tok = p.groups[3 * gi_ + 2];
+    shared_tok = (shared_tok > p.max_shared ? p.max_shared : shared_tok) & ~15;   // whole groups
+    shared_tok = shared_tok < 0 ? 0 : (shared_tok > cap ? cap : shared_tok);
+    const int G = p.Hq / p.Hkv;
+    const int M = members * G;           // query rows (host checks M <= 16 * NSET)
+    const int t0 = part * p.pre_tokens;
+    if (first < 0 || first >= p.B || t0 >= shared_tok || members <= 0) return;
+    const int ntok = min(p.pre_tokens, shared_tok - t0);
+    const int ng = (ntok + 15) >> 4;
+    const int last = ng - 1;
+
+    // table entries of the partition's groups, read from the first member's row
+    int tblv;
+    {
+        const int32_t* trow = p.tables + (int64_t)first * p.max_blocks;
+        int i = (t0 + lane * 16) >> p.bs_shift;
+        i = i < p.max_blocks ? i : p.max_blocks - 1;
+        const int e = trow[i];
+        tblv = e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);
+    }
+    const int r = lane >> 4;
+    const int c = lane & 15;
+    u32x4_t qf[NSET][NQ];
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+        const int qr = 16 * s + c;
+        if (qr < M) {
+            const int mb = qr / G, hh = qr - mb * G;
+            const char* qrow = p.q + ((int64_t)(first + mb) * p.Hq + g * G + hh) * ROW;
+#pragma unroll
+            for (int k = 0; k < NQ; ++k)
+                qf[s][k] = *reinterpret_cast<const u32x4_t*>(qrow + (k * 32 + r * 8) * 2);
+        } else {
+#pragma unroll
+            for (int k = 0; k < NQ; ++k) qf[s][k] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+
+    const int64_t tile_bytes = (int64_t)p.bs * ROW;
+    const int64_t blk_bytes = (int64_t)p.Hkv * tile_bytes;
+    const int bs_mask = p.bs - 1;
+    const char* kbase = p.k + g * tile_bytes;
+    const char* vbase = p.v + g * tile_bytes;
+    const uint32_t koff = (uint32_t)(((c >> 2) + 4 * (c & 3)) * ROW + r * 16);
+    const uint32_t voff = (uint32_t)(r * ROW + c * WV);
+    struct Item {
+        u32x4_t q[NQ];
+    };
+    auto goff = [&](int gq) -> int64_t {
+        gq = gq < last ? gq : last;
+        const int ph = __builtin_amdgcn_readlane(tblv, gq);
+        return (int64_t)ph * blk_bytes + (int64_t)((t0 + gq * 16) & bs_mask) * ROW;
+    };
+    auto issue_k = [&](int gq, Item& dst) {
+        const char* kb = kbase + goff(gq);
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) dst.q[k] = *reinterpret_cast<const u32x4_t*>(kb + koff + k * 64);
+    };
+    auto issue_v = [&](int gq, Item& dst) {
+        const char* vb = vbase + goff(gq);
+        if constexpr (WV == 16) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                dst.q[k] = *reinterpret_cast<const u32x4_t*>(vb + voff + k * 4 * ROW);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; k += 2) {
+                const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vb + voff + k * 4 * ROW);
+                const u32x2_t e = *reinterpret_cast<const u32x2_t*>(vb + voff + (k + 1) * 4 * ROW);
+                dst.q[k / 2] = __builtin_shufflevector(a, e, 0, 1, 2, 3);
+            }
+        }
+    };
+    auto vword = [&](const Item& it, int k, int w) -> uint32_t {
+        if constexpr (WV == 16) return it.q[k][w];
+        else return it.q[k >> 1][(k & 1) * 2 + w];
+    };
+
+    f32x4_t acc[NSET][EV];
+    float m_run[NSET], l_run[NSET];
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+        m_run[s] = -INFINITY;
+        l_run[s] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) acc[s][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const float cl2 = p.scale_log2;
+    Item ring[DEPTH];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_k(u, ring[2 * u]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_v(u, ring[2 * u + 1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int t0g = 0; t0g < ng; t0g += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = t0g + u;
+            Item& kit = ring[2 * u];
+            Item& vit = ring[2 * u + 1];
+            const bool live = t < ng;
+            const int valid = min(16, ntok - 16 * t);
+            float y[NSET][4];
+            uint32_t pw[NSET][2];
+            if (live) {
+#pragma unroll
+                for (int s = 0; s < NSET; ++s) {
+                    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int k = 0; k < NQ; ++k)
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, kit.q[k]),
+                            __builtin_bit_cast(bf16x8_t, qf[s][k]), sc, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y[s][i] = sc[i] * cl2;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            issue_k(t + U, kit);
+            __builtin_amdgcn_sched_barrier(0);
+            if (live) {
+#pragma unroll
+                for (int s = 0; s < NSET; ++s) {
+                    if (valid < 16) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) y[s][i] = (r + 4 * i < valid) ? y[s][i] : -INFINITY;
+                    }
+                    const float mx = fmaxf(fmaxf(y[s][0], y[s][1]), fmaxf(y[s][2], y[s][3]));
+                    const float m_new = fmaxf(m_run[s], rows_max(mx));
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_new);   // per column
+                    m_run[s] = m_new;
+                    // output rows 4r + i of this lane take the factor of column 4r + i
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float ai = __shfl(alpha, 4 * r + i);
+#pragma unroll
+                        for (int e = 0; e < EV; ++e) acc[s][e][i] *= ai;
+                    }
+                    const bf16x2_t p01 = __builtin_convertvector(
+                        (f32x2_t){__builtin_amdgcn_exp2f(y[s][0] - m_new), __builtin_amdgcn_exp2f(y[s][1] - m_new)}, bf16x2_t);
+                    const bf16x2_t p23 = __builtin_convertvector(
+                        (f32x2_t){__builtin_amdgcn_exp2f(y[s][2] - m_new), __builtin_amdgcn_exp2f(y[s][3] - m_new)}, bf16x2_t);
+                    pw[s][0] = __builtin_bit_cast(uint32_t, p01);
+                    pw[s][1] = __builtin_bit_cast(uint32_t, p23);
+                    l_run[s] = l_run[s] * alpha + ((lo_bf16(pw[s][0]) + hi_bf16(pw[s][0])) +
+                                                   (lo_bf16(pw[s][1]) + hi_bf16(pw[s][1])));
+                }
+                if (valid < 16) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        if (r + 4 * k >= valid) {
+                            if constexpr (WV == 16) {
+                                vit.q[k] = u32x4_t{0u, 0u, 0u, 0u};
+                            } else {
+                                vit.q[k >> 1][(k & 1) * 2] = 0u;
+                                vit.q[k >> 1][(k & 1) * 2 + 1] = 0u;
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int w = 0; w < WV / 4; ++w) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+                        const u32x2_t bv = {__builtin_amdgcn_perm(vword(vit, 1, w), vword(vit, 0, w), sel),
+                                            __builtin_amdgcn_perm(vword(vit, 3, w), vword(vit, 2, w), sel)};
+#pragma unroll
+                        for (int s = 0; s < NSET; ++s) {
+                            const u32x2_t av = {pw[s][0], pw[s][1]};
+                            acc[s][2 * w + h] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                                __builtin_bit_cast(s16x4_t, av), __builtin_bit_cast(s16x4_t, bv),
+                                acc[s][2 * w + h], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            issue_v(t + U, vit);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // records: query row qr = 16 s + 4 r + i sits in lane (r, c), output columns c*EV..;
+    // its (max, sum) were kept per column qr
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+        const float lcol = rows_sum(l_run[s]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int qr = 16 * s + 4 * r + i;
+            const float lr = __shfl(lcol, 4 * r + i);
+            const float mr = __shfl(m_run[s], 4 * r + i);
+            if (qr < M) {
+                const int mb = qr / G, hh = qr - mb * G;
+                const int64_t row = (int64_t)(first + mb) * p.Hq + g * G + hh;
+                float* dst = p.ws_o + (row * p.n_parts + part) * D + c * EV;
+#pragma unroll
+                for (int e = 0; e < EV; e += 4)
+                    *reinterpret_cast<float4*>(dst + e) =
+                        make_float4(acc[s][e][i], acc[s][e + 1][i], acc[s][e + 2][i], acc[s][e + 3][i]);
+                if (c == 0) p.ws_ml[row * p.n_parts + part] = make_float2(mr, lr);
             }
         }
     }
@@ -819,9 +1101,22 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
     const int cap = p.max_blocks * p.bs;
     int L = p.lens[b];
     L = L < 0 ? 0 : (L > cap ? cap : L);
-    const int np = (L + p.part_tokens - 1) / p.part_tokens;
-    if (np <= 1) return;
     const int64_t row = (int64_t)b * p.Hq + h;
+    int np;
+    if (p.groups != nullptr) {
+        // shared-prefix mode: the prefix partitions of b's group, then b's own partitions,
+        // all left as records (an empty sequence gets a zero row here)
+        int start;
+        find_group(p, b, L, &start);
+        np = (start + p.pre_tokens - 1) / p.pre_tokens + (L - start + p.part_tokens - 1) / p.part_tokens;
+        if (np == 0) {
+            for (int i = tid; i < D; i += 256) p.out[row * D + i] = 0.f;
+            return;
+        }
+    } else {
+        np = (L + p.part_tokens - 1) / p.part_tokens;
+        if (np <= 1) return;
+    }
     const float2* ml = p.ws_ml + row * p.n_parts;
     const float* wo = p.ws_o + row * p.n_parts * D;
 
@@ -1481,12 +1776,33 @@ hipError_t dispatch_d(const Params& prm, int B, int Hkv, int D, int G, void* str
     return hipErrorInvalidValue;
 }
 
+template <int D>
+hipError_t launch_shared_d(const Params& prm, int G, int nset, int n_pre, int n_suf, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const dim3 gpre(prm.n_groups * prm.Hkv * n_pre);
+    if (n_pre > 0 && prm.n_groups > 0) {
+        if (nset == 1) hipLaunchKernelGGL((decode_prefix_kernel<D, 1>), gpre, dim3(64), 0, s, prm);
+        else if (nset == 2) hipLaunchKernelGGL((decode_prefix_kernel<D, 2>), gpre, dim3(64), 0, s, prm);
+        else hipLaunchKernelGGL((decode_prefix_kernel<D, 4>), gpre, dim3(64), 0, s, prm);
+    }
+    const dim3 gsuf(n_suf * prm.Hkv * prm.B);
+    switch (G) {
+        case 1: hipLaunchKernelGGL((decode_bf16_kernel<D, 1, PA_BF16_DEPTH, PA_BF16_CHUNK, (PA_BF16_QLDS != 0), PA_BF16_WAVES>), gsuf, dim3(64 * PA_BF16_WAVES), 0, s, prm); break;
+        case 2: hipLaunchKernelGGL((decode_bf16_kernel<D, 2, PA_BF16_DEPTH, PA_BF16_CHUNK, (PA_BF16_QLDS != 0), PA_BF16_WAVES>), gsuf, dim3(64 * PA_BF16_WAVES), 0, s, prm); break;
+        case 4: hipLaunchKernelGGL((decode_bf16_kernel<D, 4, PA_BF16_DEPTH, PA_BF16_CHUNK, (PA_BF16_QLDS != 0), PA_BF16_WAVES>), gsuf, dim3(64 * PA_BF16_WAVES), 0, s, prm); break;
+        case 8: hipLaunchKernelGGL((decode_bf16_kernel<D, 8, PA_BF16_DEPTH, PA_BF16_CHUNK, (PA_BF16_QLDS != 0), PA_BF16_WAVES>), gsuf, dim3(64 * PA_BF16_WAVES), 0, s, prm); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(prm.Hq, prm.B), dim3(256), 0, s, prm);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 namespace pa_internal {
 
 int launch_decode(const DecodeLaunch& a, const char** err) {
-    Params prm;
+    Params prm{};   // zero: no shared-prefix groups, no stream records
     prm.out = a.out;
     prm.ws_o = a.ws_o;
     prm.ws_ml = reinterpret_cast<float2*>(a.ws_ml);
@@ -1528,6 +1844,47 @@ int launch_decode(const DecodeLaunch& a, const char** err) {
         e = a.kv_dtype == 1 ? dispatch_d<true>(prm, a.B, a.Hkv, a.D, G, a.stream)
                             : dispatch_d<false>(prm, a.B, a.Hkv, a.D, G, a.stream);
     }
+    if (e != hipSuccess) {
+        *err = hipGetErrorString(e);
+        return (int)e;
+    }
+    return 0;
+}
+
+int launch_decode_shared(const SharedLaunch& a, const char** err) {
+    Params prm{};
+    prm.out = a.out;
+    prm.ws_o = a.ws_o;
+    prm.ws_ml = reinterpret_cast<float2*>(a.ws_ml);
+    prm.q = static_cast<const char*>(a.q);
+    prm.k = static_cast<const char*>(a.k);
+    prm.v = static_cast<const char*>(a.v);
+    prm.tables = a.tables;
+    prm.lens = a.lens;
+    prm.B = a.B;
+    prm.Hq = a.Hq;
+    prm.Hkv = a.Hkv;
+    prm.bs = a.bs;
+    int shift = 0;
+    while ((1 << shift) < a.bs) ++shift;
+    prm.bs_shift = shift;
+    prm.num_blocks = a.num_blocks;
+    prm.max_blocks = a.max_blocks;
+    prm.part_tokens = a.part_tokens;
+    prm.n_parts = a.n_slots;
+    prm.scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+    prm.groups = a.groups;
+    prm.n_groups = a.n_groups;
+    prm.pre_tokens = a.pre_tokens;
+    prm.max_members = a.max_members;
+    prm.max_shared = a.max_shared;
+    if (a.B == 0) return 0;
+    const int G = a.Hq / a.Hkv;
+    const int m = a.max_members * G;
+    const int nset = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
+    const hipError_t e = a.D == 64 ? launch_shared_d<64>(prm, G, nset, a.n_pre, a.n_suf, a.stream)
+                       : a.D == 128 ? launch_shared_d<128>(prm, G, nset, a.n_pre, a.n_suf, a.stream)
+                                    : hipErrorInvalidValue;
     if (e != hipSuccess) {
         *err = hipGetErrorString(e);
         return (int)e;

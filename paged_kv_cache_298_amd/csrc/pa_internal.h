@@ -41,8 +41,32 @@ constexpr int kMaxStreamB = 4096;        // sequences whose prefix fits the kern
 constexpr int kMaxStreamWaves = 4096;    // resident waves the records are sized for
 constexpr int kDefaultMinSlice = 8;
 
+// Shared-prefix decode (pa_decode_shared), already validated on the host.
+struct SharedLaunch {
+    float* out;
+    float* ws_o;             // [B, Hq, n_slots, D]
+    float* ws_ml;            // [B, Hq, n_slots, 2]
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* tables;
+    const int32_t* lens;
+    const int32_t* groups;   // device [n_groups, 3]
+    int32_t n_groups, max_members, max_shared;
+    int32_t B, Hq, Hkv, D, bs, num_blocks, max_blocks;
+    int32_t pre_tokens;      // tokens per prefix partition
+    int32_t part_tokens;     // tokens per partition of the sequences' own tokens
+    int32_t n_pre, n_suf, n_slots;
+    float scale;
+    void* stream;
+};
+
+constexpr int kPrefixTokens = 256;
+constexpr int kMaxSharedRows = 64;      // members x G query rows per KV head
+
 // Each returns 0 on success or a nonzero HIP error code (message in *err).
 int launch_decode(const DecodeLaunch& a, const char** err);
+int launch_decode_shared(const SharedLaunch& a, const char** err);
 int launch_reshape_and_cache(void* k_cache, void* v_cache, const void* key, const void* value,
                              const int32_t* slot_mapping, int32_t T, int32_t Hkv,
                              int32_t row_bytes, int32_t block_size, int32_t num_blocks,

@@ -32,6 +32,9 @@ _SIGS = {
     "pa_set_partition_tokens": (_i32, [_i32]),
     "pa_set_decode_path": (_i32, [_i32]),
     "pa_set_stream_waves": (_i32, [_i32, _i32]),
+    "pa_decode_shared": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_decode_shared_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                     _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
@@ -132,6 +135,33 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, workspace
     _check(_lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                           _ptr(seq_lens), B, Hq, Hkv, D, bs, nb, max_blocks, float(scale),
                           _kv_dtype(k_cache), _ptr(workspace), ws_bytes, _stream(q, stream)))
+    return out
+
+
+def pa_decode_shared_workspace_bytes(B, Hq, D, block_size, max_blocks, max_shared_tokens):
+    return int(_lib.pa_decode_shared_workspace_bytes(B, Hq, D, block_size, max_blocks,
+                                                     max_shared_tokens))
+
+
+def pa_decode_shared(out, q, k_cache, v_cache, block_tables, seq_lens, groups, max_members,
+                     max_shared_tokens, scale, workspace=None, stream=None):
+    """pa_decode for groups of consecutive sequences sharing their leading blocks.
+    groups: int32 [n_groups, 3] on the device (first sequence, members, shared tokens),
+    sorted by first sequence; max_members / max_shared_tokens: host bounds over the groups."""
+    B, Hq, D = q.shape
+    nb, Hkv, bs, _ = k_cache.shape
+    max_blocks = block_tables.shape[1]
+    n_groups = 0 if groups is None else groups.shape[0]
+    need = pa_decode_shared_workspace_bytes(B, Hq, D, bs, max_blocks, max_shared_tokens)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.pa_decode_shared(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(block_tables), _ptr(seq_lens),
+                                 _ptr(groups) if n_groups else None, n_groups, int(max_members),
+                                 int(max_shared_tokens), B, Hq, Hkv, D, bs, nb, max_blocks,
+                                 float(scale), _kv_dtype(k_cache), _ptr(workspace), ws_bytes,
+                                 _stream(q, stream)))
     return out
 
 

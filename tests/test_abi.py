@@ -171,3 +171,39 @@ def test_python_binding_marshals_dtypes():
     assert pa._kv_dtype(torch.zeros(1, dtype=torch.bfloat16)) == pa.PA_BF16
     with pytest.raises(ValueError):
         pa._ptr(torch.zeros(4, 4).t())
+
+
+def _shared(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, groups=FAKE, ng=2, mm=4,
+             msh=64, B=8, Hq=32, Hkv=8, D=128, bs=16, nb=64, mb=8, scale=0.1, dt=pa.PA_BF16,
+             ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return pa._lib.pa_decode_shared(a["out"], a["q"], a["k"], a["v"], a["bt"], a["sl"], a["groups"],
+                                    a["ng"], a["mm"], a["msh"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                    a["bs"], a["nb"], a["mb"], a["scale"], a["dt"], a["ws"], a["wsb"],
+                                    a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=pa.PA_F32), pa.PA_ERR_UNSUPPORTED),          # bf16 only
+    (dict(bs=8), pa.PA_ERR_UNSUPPORTED),
+    (dict(mm=17), pa.PA_ERR_UNSUPPORTED),                 # 17 x 4 query rows > 64
+    (dict(groups=None), pa.PA_ERR_INVALID_ARG),
+    (dict(ng=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(msh=16 * 8 + 1), pa.PA_ERR_INVALID_ARG),        # past the table capacity
+    (dict(), pa.PA_ERR_INVALID_ARG),                      # no workspace
+    (dict(ws=FAKE, wsb=16), pa.PA_ERR_INVALID_ARG),
+])
+def test_decode_shared_rejects_bad_arguments(kw, status):
+    assert _shared(**kw) == status
+    assert pa._lib.pa_last_error().decode().startswith("pa_decode_shared")
+
+
+def test_decode_shared_workspace_and_empty_batch():
+    assert _shared(B=0, out=None, q=None) == pa.PA_OK
+    # slots: ceil(shared / 256) prefix partitions + ceil(capacity / partition) own ones
+    P = pa.pa_decode_partition_tokens(16, 144)
+    n = -(-2032 // 256) + -(-16 * 144 // P)
+    rows = 128 * 32 * n
+    assert pa.pa_decode_shared_workspace_bytes(128, 32, 128, 16, 144, 2032) == _up(rows * 128 * 4) + rows * 8
+    assert pa.pa_decode_shared_workspace_bytes(0, 32, 128, 16, 144, 2032) == 0

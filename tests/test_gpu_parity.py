@@ -378,6 +378,84 @@ def test_placement_invariance_new_block_sizes(pa, bs):
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
 
+# ------------------------------------------------------------------ shared prefixes
+
+def _shared_step(pa, wl, groups, max_members, max_shared):
+    """copy_blocks -> reshape_and_cache -> pa_decode_shared, on the current stream."""
+    from tests._gpu_helpers import to_dev
+    dw = DevWorkload(wl)
+    if dw.pairs is not None:
+        pa.pa_copy_blocks(dw.k, dw.v, dw.pairs)
+    pa.pa_reshape_and_cache(dw.k, dw.v, dw.nk, dw.nv, dw.slots)
+    g = to_dev(np.asarray(groups, np.int32).reshape(-1, 3)) if len(groups) else None
+    pa.pa_decode_shared(dw.out, dw.q, dw.k, dw.v, dw.bt, dw.sl, g, max_members, max_shared,
+                        wl.scale)
+    torch.cuda.synchronize()
+    return dw.out.cpu().numpy()
+
+
+def _shared_parity(pa, oracle, wl, groups, max_members, max_shared, tag):
+    note(f"shared prefix {tag}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} bs={wl.block_size} "
+         f"groups={groups[:2]}...")
+    got = _shared_step(pa, wl, groups, max_members, max_shared)
+    ref, _, _ = oracle_step(oracle, wl)
+    err = max_err(got, ref)
+    note(f"  max abs err {err:.3e}")
+    assert err <= TOL[wl.dtype]
+    return got
+
+
+SHARED = [
+    # prompts, candidates, prompt tokens, extra tokens, Hq, Hkv, D, bs
+    (3, 4, 512, 40, 32, 8, 128, 16),
+    (2, 8, 256, 300, 64, 8, 128, 32),      # G = 8, 8 members: 64 query rows per KV head
+    (2, 3, 384, 20, 16, 4, 64, 16),        # D = 64
+    (2, 2, 1024, 100, 32, 8, 128, 128),    # 128-token blocks
+]
+
+
+@pytest.mark.parametrize("case", SHARED, ids=lambda c: f"p{c[0]}x{c[1]}-L{c[2]}-G{c[4] // c[5]}-D{c[6]}-bs{c[7]}")
+def test_shared_prefix_decode(pa, oracle, case):
+    npr, nc, plen, extra, Hq, Hkv, D, bs = case
+    wl = W.make_shared_prefix("sp", npr, nc, plen, extra, Hq, Hkv, D, bs, W.BF16, seed=plen + bs)
+    shared = plen - bs                       # the last prompt block is cloned per candidate
+    groups = [(p * nc, nc, shared) for p in range(npr)]
+    _shared_parity(pa, oracle, wl, groups, nc, shared, "all prompts")
+
+
+def test_shared_prefix_mixed_members_and_rounding(pa, oracle):
+    """Only some prompts form groups (the others are read per sequence), a shared count that
+    is not a multiple of 16 (used as 480), and one member with no tokens of its own."""
+    wl = W.make_shared_prefix("mix", 3, 4, 512, 60, 32, 8, 128, 16, W.BF16, seed=9)
+    wl.seq_lens[9] = 496 - 7 - 2             # member of the third group: L = 487 > 480
+    wl.seq_lens[8] = 480                     # exactly the rounded shared tokens
+    groups = [(0, 4, 496), (8, 4, 489)]
+    _shared_parity(pa, oracle, wl, groups, 4, 496, "mixed")
+
+
+def test_shared_prefix_no_groups_is_plain_decode(pa, oracle):
+    wl = W.make_shared_prefix("none", 2, 4, 256, 30, 32, 8, 128, 16, W.BF16, seed=3)
+    _shared_parity(pa, oracle, wl, [], 1, 0, "no groups")
+
+
+def test_shared_prefix_config3_full(pa, oracle):
+    wl = W.config(3)
+    nc, shared = 8, 2048 - 16
+    groups = [(p * nc, nc, shared) for p in range(16)]
+    got = _shared_parity(pa, oracle, wl, groups, nc, shared, "config 3")
+    dw = DevWorkload(wl)
+    plain = gpu_step(pa, dw)                  # the same rows through pa_decode
+    assert float(np.max(np.abs(plain - got))) <= TOL[wl.dtype]
+
+
+def test_shared_prefix_repeatable(pa):
+    outs = []
+    for seed in (21, 21):
+        wl = W.make_shared_prefix("inv", 2, 4, 512, 40, 32, 8, 128, 16, W.BF16, seed=seed)
+        outs.append(_shared_step(pa, wl, [(0, 4, 496), (4, 4, 496)], 4, 496))
+    assert np.array_equal(outs[0], outs[1])
+
+
 def test_one_token_returns_its_value_exactly(pa):
     for dt in (W.F32, W.BF16):
         wl = W.make_workload("one", 3, 8, 2, 128, 16, [1, 1, 1], dt, seed=5, keep_logical=True)
