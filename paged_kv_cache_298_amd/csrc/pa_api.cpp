@@ -333,7 +333,9 @@ int32_t pa_decode_shared(float* out, const void* q, const void* k_cache, const v
                     sw.total, workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 256))
         return fail(PA_ERR_INVALID_ARG, "pa_decode_shared: workspace must be 256-byte aligned");
-    if ((int64_t)n_groups * Hkv * sw.n_pre > 0x7fffffff || (int64_t)sw.n_suf * Hkv * B > 0x7fffffff)
+    // one launch of four items per block: the prefix items, then the suffix partitions
+    const int64_t pre_items = (int64_t)n_groups * Hkv * sw.n_pre, suf_items = (int64_t)sw.n_suf * Hkv * B;
+    if (pre_items > 0x7fffffff || suf_items > 0x7fffffff || (pre_items + 3) / 4 + (suf_items + 3) / 4 > 0x7fffffff)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared: work items exceed the grid limit");
 
     pa_internal::SharedLaunch a;

@@ -47,6 +47,12 @@
 #ifndef PA_BF16_QLDS
 #define PA_BF16_QLDS 0
 #endif
+#ifndef PA_SHARED_DEPTH
+#define PA_SHARED_DEPTH 4
+#endif
+#ifndef PA_SHARED_CHUNK
+#define PA_SHARED_CHUNK 4
+#endif
 #ifndef PA_BF16_WAVES
 #define PA_BF16_WAVES 4
 #endif
@@ -95,30 +101,44 @@ struct Params {
     int pre_tokens;          // tokens per prefix partition
     int max_members;         // host bounds the device groups are clamped to (they size the
     int max_shared;          // workspace and the query tiles)
+    int pre_items;           // prefix items (group, KV head, partition) of a fused launch
+    int pre_blocks;          // blocks holding them, four items each
+    int suf_items;           // suffix partitions of a fused launch
 };
 
 // Shared-prefix mode: the group holding sequence b (groups are sorted by first sequence
 // and disjoint), or -1; *start = the tokens b shares with its group (0 when none), clamped
-// into [0, L].
+// into [0, L]. Called by all 64 lanes of a wave with the same b: a 64-way search in which
+// each lane tests one candidate per step, so up to 64 groups cost one memory round trip
+// and up to 4096 two (a binary search would pay one per halving). Members are clamped to
+// the host bound, as the prefix kernel clamps them.
 __device__ __forceinline__ int find_group(const Params& p, int b, int L, int* start) {
-    int lo = 0, hi = p.n_groups - 1, found = -1;
-    while (lo <= hi) {
-        const int mid = (lo + hi) >> 1;
-        if (p.groups[3 * mid] <= b) {
-            found = mid;
-            lo = mid + 1;
-        } else {
-            hi = mid - 1;
-        }
+    const int lane = threadIdx.x & 63;
+    int lo = 0, n = p.n_groups;   // candidates lo .. lo + n - 1
+    int found = -1, first = 0, members = 0, sh = 0;
+    while (n > 0) {
+        const int stride = (n + 63) >> 6;
+        const bool in = lane * stride < n;
+        const int32_t* gp = p.groups + 3 * (lo + (in ? lane * stride : 0));
+        const int f = gp[0], mm = gp[1], ss = gp[2];   // one round trip for all three
+        const uint64_t m = __ballot(in && f <= b);
+        if (m == 0) break;
+        const int k = 63 - __builtin_clzll(m);           // last candidate starting <= b
+        found = lo + k * stride;
+        first = __builtin_amdgcn_readlane(f, k);
+        members = __builtin_amdgcn_readlane(mm, k);
+        sh = __builtin_amdgcn_readlane(ss, k);
+        if (stride == 1) break;
+        const int end = lo + n;
+        lo = found + 1;
+        n = min(stride - 1, end - lo);
     }
     *start = 0;
-    if (found >= 0 && b < p.groups[3 * found] + p.groups[3 * found + 1]) {
-        int sh = p.groups[3 * found + 2];
-        sh = (sh > p.max_shared ? p.max_shared : sh) & ~15;   // whole 16-token groups only
-        *start = sh < 0 ? 0 : (sh > L ? L : sh);
-        return found;
-    }
-    return -1;
+    members = members > p.max_members ? p.max_members : members;
+    if (found < 0 || b < first || b - first >= members) return -1;
+    sh = (sh > p.max_shared ? p.max_shared : sh) & ~15;   // whole 16-token groups only
+    *start = sh < 0 ? 0 : (sh > L ? L : sh);
+    return found;
 }
 
 __device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u << 16); }
@@ -176,8 +196,7 @@ __device__ __forceinline__ void wave_sync() {
 // every XCD the same mix of heads, sequences and partitions: with 8 KV heads, XCD k serves
 // KV head k of every partition, an exact eighth of the bytes. (Partition-fastest order
 // would send every sequence's first partition, the one that always exists, to one XCD.)
-__device__ __forceinline__ void work_item(const Params& p, int& g, int& b, int& part) {
-    const int id = blockIdx.x;
+__device__ __forceinline__ void work_item(const Params& p, int id, int& g, int& b, int& part) {
     g = id % p.Hkv;
     const int rest = id / p.Hkv;
     b = rest % p.B;
@@ -218,7 +237,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(Params p) {
 
     const int lane = threadIdx.x;
     int g, b, part;
-    work_item(p, g, b, part);
+    work_item(p, blockIdx.x, g, b, part);
     const int cap = p.max_blocks * p.bs;
     int L = p.lens[b];
     L = L < 0 ? 0 : (L > cap ? cap : L);
@@ -489,7 +508,7 @@ __device__ __forceinline__ float quad_bcast(float v, int m) {
 }
 
 template <int D, int G, int DEPTH, int kChunk, bool QLDS, int W>
-__global__ __launch_bounds__(64 * W) void decode_bf16_kernel(Params p) {
+__device__ __forceinline__ void bf16_item(const Params& p, int id) {
     constexpr int ROW = D * 2;              // bytes per cached row
     constexpr int NQ = D / 32;              // 16-byte registers per ring item
     constexpr int WV = D / 8;               // bytes of a V row per lane per load (16 or 8)
@@ -502,9 +521,9 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(Params p) {
     static_assert(kChunk % DEPTH == 0, "the ring depth must divide the chunk");
 
     const int lane = threadIdx.x & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave in the group
+    const int wid = W == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave in the group
     int g, b, part;
-    work_item(p, g, b, part);
+    work_item(p, id, g, b, part);
     const int cap = p.max_blocks * p.bs;
     int L = p.lens[b];
     L = L < 0 ? 0 : (L > cap ? cap : L);
@@ -842,6 +861,11 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(Params p) {
     }
 }
 
+template <int D, int G, int DEPTH, int kChunk, bool QLDS, int W>
+__global__ __launch_bounds__(64 * W) void decode_bf16_kernel(Params p) {
+    bf16_item<D, G, DEPTH, kChunk, QLDS, W>(p, blockIdx.x);
+}
+
 
 // Shared prefix (parallel sampling, shared prompts): the leading tokens a group of
 // sequences shares are read once for all of them. One wavefront per (group, KV head,
@@ -854,7 +878,7 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(Params p) {
 // (member, head) gets a partial record in slot `part`; the partition merge combines them
 // with the members' own tokens.
 template <int D, int NSET>
-__global__ __launch_bounds__(64) void decode_prefix_kernel(Params p) {
+__device__ __forceinline__ void prefix_item(const Params& p, int id) {
     constexpr int ROW = D * 2;
     constexpr int NQ = D / 32;
     constexpr int WV = D / 8;
@@ -863,8 +887,7 @@ __global__ __launch_bounds__(64) void decode_prefix_kernel(Params p) {
     constexpr int U = DEPTH / 2;
     static_assert(D == 64 || D == 128, "head size");
 
-    const int lane = threadIdx.x;
-    const int id = blockIdx.x;
+    const int lane = threadIdx.x & 63;
     const int g = id % p.Hkv;
     const int rest = id / p.Hkv;
     const int gi_ = rest % p.n_groups;
@@ -1085,15 +1108,34 @@ __global__ __launch_bounds__(64) void decode_prefix_kernel(Params p) {
     }
 }
 
+// The prefix partitions and the members' own tokens in one launch of 4-wave blocks, one
+// item per wave: blocks below pre_blocks hold the prefix items (first, so that the longest
+// work starts earliest), the rest the suffix partitions. A suffix partition is short (the
+// tokens a member added after the shared prefix), so it gets a single wave and a small
+// chunk, which starts its V loads after four K tiles rather than eight.
+template <int D, int G, int NSET>
+__global__ __launch_bounds__(256) void decode_shared_kernel(Params p) {
+    const int bid = blockIdx.x;
+    const int item = (bid < p.pre_blocks ? bid : bid - p.pre_blocks) * 4 + (int)(threadIdx.x >> 6);
+    if (bid < p.pre_blocks) {
+        if (item < p.pre_items) prefix_item<D, NSET>(p, item);
+    } else if (item < p.suf_items) {
+        bf16_item<D, G, PA_SHARED_DEPTH, PA_SHARED_CHUNK, false, 1>(p, item);
+    }
+}
+
 // Combine the partitions of one (sequence, query head):
 // out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i, with M = max_i m_i.
+// Thread (pg, c4) folds partitions pg, pg + NPG, ... of float4 column c4, four per batch
+// whose loads issue together (indices past the last are clamped to a valid record and
+// weighted 0), rescaling its running sum when the maximum grows; the NPG partial sums
+// then meet in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
     constexpr int C4 = D / 4;          // float4 columns
     constexpr int NPG = 256 / C4;      // partition groups per block
-    __shared__ float red_m[4];
     __shared__ float4 red_o[NPG][C4];
-    __shared__ float red_l[NPG];
+    __shared__ float2 red_ml[NPG];
 
     const int h = blockIdx.x;
     const int b = blockIdx.y;
@@ -1120,42 +1162,61 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
     const float2* ml = p.ws_ml + row * p.n_parts;
     const float* wo = p.ws_o + row * p.n_parts * D;
 
-    float mx = -INFINITY;
-    for (int i = tid; i < np; i += 256) mx = fmaxf(mx, ml[i].x);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if ((tid & 63) == 0) red_m[tid >> 6] = mx;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-
     const int c4 = tid % C4;
     const int pg = tid / C4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float den = 0.f;
-    for (int i = pg; i < np; i += NPG) {
-        const float2 mli = ml[i];
-        const float w = __builtin_amdgcn_exp2f(mli.x - M);
-        const float4 o = reinterpret_cast<const float4*>(wo + (int64_t)i * D)[c4];
-        acc.x = fmaf(w, o.x, acc.x);
-        acc.y = fmaf(w, o.y, acc.y);
-        acc.z = fmaf(w, o.z, acc.z);
-        acc.w = fmaf(w, o.w, acc.w);
-        den = fmaf(w, mli.y, den);
+    float den = 0.f, m = -INFINITY;
+    for (int i0 = pg; i0 < np; i0 += 4 * NPG) {
+        float2 mlv[4];
+        float4 ov[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * NPG;
+            const int ic = i < np ? i : i0;
+            mlv[u] = ml[ic];
+            ov[u] = reinterpret_cast<const float4*>(wo + (int64_t)ic * D)[c4];
+            if (i >= np) mlv[u].x = -INFINITY;
+        }
+        float mn = m;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mn = fmaxf(mn, mlv[u].x);
+        const float a = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first batch
+        acc.x *= a; acc.y *= a; acc.z *= a; acc.w *= a;
+        den *= a;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float w = __builtin_amdgcn_exp2f(mlv[u].x - mn);
+            acc.x = fmaf(w, ov[u].x, acc.x);
+            acc.y = fmaf(w, ov[u].y, acc.y);
+            acc.z = fmaf(w, ov[u].z, acc.z);
+            acc.w = fmaf(w, ov[u].w, acc.w);
+            den = fmaf(w, mlv[u].y, den);
+        }
+        m = mn;
     }
     red_o[pg][c4] = acc;
-    if (c4 == 0) red_l[pg] = den;
+    if (c4 == 0) red_ml[pg] = make_float2(m, den);
     __syncthreads();
     if (pg == 0) {
-        float4 s = red_o[0][c4];
-        float dsum = red_l[0];
-        for (int j = 1; j < NPG; ++j) {
+        float M = red_ml[0].x;
+#pragma unroll
+        for (int j = 1; j < NPG; ++j) M = fmaxf(M, red_ml[j].x);
+        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+        float dsum = 0.f;
+#pragma unroll
+        for (int j = 0; j < NPG; ++j) {
+            const float2 mlj = red_ml[j];
+            const float w = __builtin_amdgcn_exp2f(mlj.x - M);   // 0 for a group with none
             const float4 x = red_o[j][c4];
-            s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
-            dsum += red_l[j];
+            sum.x = fmaf(w, x.x, sum.x);
+            sum.y = fmaf(w, x.y, sum.y);
+            sum.z = fmaf(w, x.z, sum.z);
+            sum.w = fmaf(w, x.w, sum.w);
+            dsum = fmaf(w, mlj.y, dsum);
         }
         const float inv = 1.0f / dsum;
         reinterpret_cast<float4*>(p.out + row * D)[c4] =
-            make_float4(s.x * inv, s.y * inv, s.z * inv, s.w * inv);
+            make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
     }
 }
 
@@ -1776,23 +1837,30 @@ hipError_t dispatch_d(const Params& prm, int B, int Hkv, int D, int G, void* str
     return hipErrorInvalidValue;
 }
 
+template <int D, int G>
+hipError_t launch_fused(const Params& prm, int nset, int n_suf, hipStream_t s) {
+    const dim3 grid(prm.pre_blocks + (prm.suf_items + 3) / 4);
+    if (nset == 1) hipLaunchKernelGGL((decode_shared_kernel<D, G, 1>), grid, dim3(256), 0, s, prm);
+    else if (nset == 2) hipLaunchKernelGGL((decode_shared_kernel<D, G, 2>), grid, dim3(256), 0, s, prm);
+    else hipLaunchKernelGGL((decode_shared_kernel<D, G, 4>), grid, dim3(256), 0, s, prm);
+    return hipSuccess;
+}
+
 template <int D>
-hipError_t launch_shared_d(const Params& prm, int G, int nset, int n_pre, int n_suf, void* stream) {
+hipError_t launch_shared_d(Params prm, int G, int nset, int n_pre, int n_suf, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const dim3 gpre(prm.n_groups * prm.Hkv * n_pre);
-    if (n_pre > 0 && prm.n_groups > 0) {
-        if (nset == 1) hipLaunchKernelGGL((decode_prefix_kernel<D, 1>), gpre, dim3(64), 0, s, prm);
-        else if (nset == 2) hipLaunchKernelGGL((decode_prefix_kernel<D, 2>), gpre, dim3(64), 0, s, prm);
-        else hipLaunchKernelGGL((decode_prefix_kernel<D, 4>), gpre, dim3(64), 0, s, prm);
-    }
-    const dim3 gsuf(n_suf * prm.Hkv * prm.B);
+    prm.pre_items = prm.n_groups * prm.Hkv * n_pre;
+    prm.pre_blocks = (prm.pre_items + 3) / 4;
+    prm.suf_items = n_suf * prm.Hkv * prm.B;
+    hipError_t e;
     switch (G) {
-        case 1: hipLaunchKernelGGL((decode_bf16_kernel<D, 1, PA_BF16_DEPTH, PA_BF16_CHUNK, (PA_BF16_QLDS != 0), PA_BF16_WAVES>), gsuf, dim3(64 * PA_BF16_WAVES), 0, s, prm); break;
-        case 2: hipLaunchKernelGGL((decode_bf16_kernel<D, 2, PA_BF16_DEPTH, PA_BF16_CHUNK, (PA_BF16_QLDS != 0), PA_BF16_WAVES>), gsuf, dim3(64 * PA_BF16_WAVES), 0, s, prm); break;
-        case 4: hipLaunchKernelGGL((decode_bf16_kernel<D, 4, PA_BF16_DEPTH, PA_BF16_CHUNK, (PA_BF16_QLDS != 0), PA_BF16_WAVES>), gsuf, dim3(64 * PA_BF16_WAVES), 0, s, prm); break;
-        case 8: hipLaunchKernelGGL((decode_bf16_kernel<D, 8, PA_BF16_DEPTH, PA_BF16_CHUNK, (PA_BF16_QLDS != 0), PA_BF16_WAVES>), gsuf, dim3(64 * PA_BF16_WAVES), 0, s, prm); break;
+        case 1: e = launch_fused<D, 1>(prm, nset, n_suf, s); break;
+        case 2: e = launch_fused<D, 2>(prm, nset, n_suf, s); break;
+        case 4: e = launch_fused<D, 4>(prm, nset, n_suf, s); break;
+        case 8: e = launch_fused<D, 8>(prm, nset, n_suf, s); break;
         default: return hipErrorInvalidValue;
     }
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(prm.Hq, prm.B), dim3(256), 0, s, prm);
     return hipGetLastError();
 }

@@ -61,7 +61,10 @@ struct SharedLaunch {
     void* stream;
 };
 
-constexpr int kPrefixTokens = 256;
+#ifndef PA_PREFIX_TOKENS
+#define PA_PREFIX_TOKENS 256
+#endif
+constexpr int kPrefixTokens = PA_PREFIX_TOKENS;
 constexpr int kMaxSharedRows = 64;      // members x G query rows per KV head
 
 // Each returns 0 on success or a nonzero HIP error code (message in *err).

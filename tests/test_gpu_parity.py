@@ -433,6 +433,15 @@ def test_shared_prefix_mixed_members_and_rounding(pa, oracle):
     _shared_parity(pa, oracle, wl, groups, 4, 496, "mixed")
 
 
+def test_shared_prefix_many_groups(pa, oracle):
+    """More than 64 groups (the group search then takes more than one step), with prompts
+    left out of every third group so that some sequences fall between groups."""
+    wl = W.make_shared_prefix("many", 100, 2, 64, 20, 8, 2, 64, 16, W.BF16, seed=5)
+    groups = [(p * 2, 2, 48) for p in range(100) if p % 3 != 1]
+    assert len(groups) > 64
+    _shared_parity(pa, oracle, wl, groups, 2, 48, "many groups")
+
+
 def test_shared_prefix_no_groups_is_plain_decode(pa, oracle):
     wl = W.make_shared_prefix("none", 2, 4, 256, 30, 32, 8, 128, 16, W.BF16, seed=3)
     _shared_parity(pa, oracle, wl, [], 1, 0, "no groups")
