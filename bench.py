@@ -141,6 +141,84 @@ def _sweep_block_size(torch, pa, W, dev, args):
             torch.cuda.empty_cache()
 
 
+def _per_call_us(torch, fn, reps, steps, warmup, stream):
+    """Mean, p10, p50 and p90 of fn's duration in us: HIP events around each call on its
+    stream, rotating over the replicas."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(warmup):
+        fn(reps[i % len(reps)])
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(reps[i % len(reps)])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return {"mean": round(float(us.mean()), 2), "p10": round(float(np.percentile(us, 10)), 2),
+            "p50": round(float(np.median(us)), 2), "p90": round(float(np.percentile(us, 90)), 2)}
+
+
+def _shared_prefix(torch, pa, W, dev, args):
+    """The shared-prefix batch (16 prompts of 2048 tokens, 8 candidates each): the step
+    copy_blocks + reshape_and_cache + pa_decode_shared, and the decode alone through
+    pa_decode_shared and through pa_decode; one JSON line. Logical bytes count every
+    sequence's tokens; unique bytes count each shared block once."""
+    wl = W.config(3, poison=False)
+    groups = wl.share_groups
+    max_members, max_shared = int(groups[:, 1].max()), int(groups[:, 2].max())
+    shared_of = np.zeros(wl.B, np.int64)
+    for first, members, sh in groups:
+        shared_of[first:first + members] = sh
+    row = wl.Hkv * wl.D * 2 * 2
+    unique = (int(groups[:, 2].astype(np.int64).sum()) + int((wl.seq_lens - shared_of).sum())) * row
+    logical = wl.kv_bytes()
+    per_replica = 2 * wl.k_cache.nbytes + wl.q.nbytes + wl.block_tables.nbytes
+    R = args.replicas or max(2, math.ceil((1 << 30) / per_replica))
+    ws_sh = pa.pa_decode_shared_workspace_bytes(wl.B, wl.Hq, wl.D, wl.block_size, wl.max_blocks,
+                                                max_shared)
+    ws_pl = pa.pa_decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.block_size, wl.max_blocks,
+                                         pa.PA_BF16)
+    _log(f"{wl.name}: B={wl.B} logical={logical} unique={unique} replicas={R}")
+    reps = [dict(q=_to_dev(wl.q, torch, dev), k=_to_dev(wl.k_cache, torch, dev),
+                 v=_to_dev(wl.v_cache, torch, dev), bt=_to_dev(wl.block_tables, torch, dev),
+                 sl=_to_dev(wl.seq_lens, torch, dev), nk=_to_dev(wl.new_key, torch, dev),
+                 nv=_to_dev(wl.new_value, torch, dev), slots=_to_dev(wl.slot_mapping, torch, dev),
+                 pairs=_to_dev(wl.cow_pairs, torch, dev), groups=_to_dev(groups, torch, dev),
+                 out=torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev),
+                 ws_sh=torch.zeros(max(ws_sh, 1), dtype=torch.uint8, device=dev),
+                 ws_pl=torch.zeros(max(ws_pl, 1), dtype=torch.uint8, device=dev))
+            for _ in range(R)]
+    stream = torch.cuda.current_stream(dev)
+
+    def shared(r):
+        pa.pa_decode_shared(r["out"], r["q"], r["k"], r["v"], r["bt"], r["sl"], r["groups"],
+                            max_members, max_shared, wl.scale, workspace=r["ws_sh"], stream=stream)
+
+    def plain(r):
+        pa.pa_decode(r["out"], r["q"], r["k"], r["v"], r["bt"], r["sl"], wl.scale,
+                     workspace=r["ws_pl"], stream=stream)
+
+    def step(r):
+        pa.pa_copy_blocks(r["k"], r["v"], r["pairs"], stream=stream)
+        pa.pa_reshape_and_cache(r["k"], r["v"], r["nk"], r["nv"], r["slots"], stream=stream)
+        shared(r)
+
+    steps = max(20, min(args.steps, 200))
+    st = _per_call_us(torch, step, reps, steps, args.warmup, stream)
+    sh = _per_call_us(torch, shared, reps, steps, args.warmup, stream)
+    pl = _per_call_us(torch, plain, reps, steps, args.warmup, stream)
+    print(json.dumps({
+        "bench": "shared_prefix", "workload": W.CONFIG_NAMES[3], "replicas_rotated": R,
+        "groups": int(len(groups)), "members": max_members, "shared_tokens": max_shared,
+        "logical_kv_bytes": logical, "unique_kv_bytes": unique,
+        "step_us": st, "decode_shared_us": sh, "decode_us": pl,
+        "shared_logical_GBps": round(logical / (sh["mean"] * 1e-6) / 1e9, 1),
+        "shared_unique_GBps": round(unique / (sh["mean"] * 1e-6) / 1e9, 1),
+        "plain_logical_GBps": round(logical / (pl["mean"] * 1e-6) / 1e9, 1),
+        "speedup_vs_pa_decode": round(pl["mean"] / sh["mean"], 3)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +234,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run pa_copy_blocks over a known number of bytes (the reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and print them")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="the shared-prefix batch through pa_decode_shared and pa_decode; "
+                         "one JSON line")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -174,6 +255,9 @@ def main():
         return
     if args.sweep_block_size:
         _sweep_block_size(torch, pa, W, dev, args)
+        return
+    if args.shared_prefix:
+        _shared_prefix(torch, pa, W, dev, args)
         return
     _log(f"generating workload {args.config}")
     wl = W.config(args.config, poison=False)

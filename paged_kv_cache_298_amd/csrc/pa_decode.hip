@@ -106,13 +106,14 @@ struct Params {
     int suf_items;           // suffix partitions of a fused launch
 };
 
-// Shared-prefix mode: the group holding sequence b (groups are sorted by first sequence
-// and disjoint), or -1; *start = the tokens b shares with its group (0 when none), clamped
-// into [0, L]. Called by all 64 lanes of a wave with the same b: a 64-way search in which
-// each lane tests one candidate per step, so up to 64 groups cost one memory round trip
-// and up to 4096 two (a binary search would pay one per halving). Members are clamped to
-// the host bound, as the prefix kernel clamps them.
-__device__ __forceinline__ int find_group(const Params& p, int b, int L, int* start) {
+// Shared-prefix mode: the tokens sequence b shares with its group (groups are sorted by
+// first sequence and disjoint), rounded down to whole 16-token groups and clamped to the
+// host bound; 0 when b is in no group. The caller clamps it to b's length. Called by all
+// 64 lanes of a wave with the same b: a 64-way search in which each lane tests one
+// candidate per step, so up to 64 groups cost one memory round trip and up to 4096 two (a
+// binary search would pay one per halving). Members are clamped to the host bound, as
+// the prefix kernel clamps them.
+__device__ __forceinline__ int group_shared(const Params& p, int b) {
     const int lane = threadIdx.x & 63;
     int lo = 0, n = p.n_groups;   // candidates lo .. lo + n - 1
     int found = -1, first = 0, members = 0, sh = 0;
@@ -120,7 +121,10 @@ __device__ __forceinline__ int find_group(const Params& p, int b, int L, int* st
         const int stride = (n + 63) >> 6;
         const bool in = lane * stride < n;
         const int32_t* gp = p.groups + 3 * (lo + (in ? lane * stride : 0));
-        const int f = gp[0], mm = gp[1], ss = gp[2];   // one round trip for all three
+        int f = gp[0], mm = gp[1], ss = gp[2];
+        // all three fields arrive in one round trip: keep the compiler from deferring the
+        // loads of the two used only once a candidate is found
+        asm volatile("" : "+v"(f), "+v"(mm), "+v"(ss));
         const uint64_t m = __ballot(in && f <= b);
         if (m == 0) break;
         const int k = 63 - __builtin_clzll(m);           // last candidate starting <= b
@@ -133,12 +137,10 @@ __device__ __forceinline__ int find_group(const Params& p, int b, int L, int* st
         lo = found + 1;
         n = min(stride - 1, end - lo);
     }
-    *start = 0;
     members = members > p.max_members ? p.max_members : members;
-    if (found < 0 || b < first || b - first >= members) return -1;
+    if (found < 0 || b < first || b - first >= members) return 0;
     sh = (sh > p.max_shared ? p.max_shared : sh) & ~15;   // whole 16-token groups only
-    *start = sh < 0 ? 0 : (sh > L ? L : sh);
-    return found;
+    return sh < 0 ? 0 : sh;
 }
 
 __device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u << 16); }
@@ -533,7 +535,7 @@ __device__ __forceinline__ void bf16_item(const Params& p, int id) {
     const bool shared = p.groups != nullptr;
     int start = 0, slot0 = 0;
     if (shared) {
-        find_group(p, b, L, &start);
+        start = min(group_shared(p, b), L);
         slot0 = (start + p.pre_tokens - 1) / p.pre_tokens;
     }
     const int t0 = start + part * p.part_tokens;
@@ -1126,10 +1128,12 @@ __global__ __launch_bounds__(256) void decode_shared_kernel(Params p) {
 
 // Combine the partitions of one (sequence, query head):
 // out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i, with M = max_i m_i.
-// Thread (pg, c4) folds partitions pg, pg + NPG, ... of float4 column c4, four per batch
-// whose loads issue together (indices past the last are clamped to a valid record and
-// weighted 0), rescaling its running sum when the maximum grows; the NPG partial sums
-// then meet in LDS.
+// Thread (pg, c4) folds partitions pg, pg + NPG, ... of float4 column c4, four per batch,
+// rescaling its running sum when the maximum grows; the NPG partial sums then meet in
+// LDS. The first batch is loaded before the partition count is known, together with the
+// length (and group) that give it: slots below n_parts always lie in the row's workspace,
+// and a slot past the count is dropped by a select, never weighted, since it may hold
+// anything.
 template <int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
     constexpr int C4 = D / 4;          // float4 columns
@@ -1140,16 +1144,37 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
     const int h = blockIdx.x;
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
-    const int cap = p.max_blocks * p.bs;
-    int L = p.lens[b];
-    L = L < 0 ? 0 : (L > cap ? cap : L);
+    const int c4 = tid % C4;
+    const int pg = tid / C4;
     const int64_t row = (int64_t)b * p.Hq + h;
+    const float2* ml = p.ws_ml + row * p.n_parts;
+    const float* wo = p.ws_o + row * p.n_parts * D;
+    float2 mlv[4];
+    float4 ov[4];
+    auto load_batch = [&](int i0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            int i = i0 + u * NPG;
+            i = i < p.n_parts ? i : 0;
+            mlv[u] = ml[i];
+            ov[u] = reinterpret_cast<const float4*>(wo + (int64_t)i * D)[c4];
+        }
+    };
+    load_batch(pg);
+
+    // the length through a vector load (b copied into a VGPR) that the group search's
+    // loads follow without a wait: a scalar load would be waited for first
+    int bv;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(bv) : "s"(b));
+    const int L_raw = p.lens[bv];
+    const int sh = p.groups != nullptr ? group_shared(p, b) : 0;
+    const int cap = p.max_blocks * p.bs;
+    const int L = L_raw < 0 ? 0 : (L_raw > cap ? cap : L_raw);
     int np;
     if (p.groups != nullptr) {
         // shared-prefix mode: the prefix partitions of b's group, then b's own partitions,
         // all left as records (an empty sequence gets a zero row here)
-        int start;
-        find_group(p, b, L, &start);
+        const int start = min(sh, L);
         np = (start + p.pre_tokens - 1) / p.pre_tokens + (L - start + p.part_tokens - 1) / p.part_tokens;
         if (np == 0) {
             for (int i = tid; i < D; i += 256) p.out[row * D + i] = 0.f;
@@ -1159,38 +1184,28 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
         np = (L + p.part_tokens - 1) / p.part_tokens;
         if (np <= 1) return;
     }
-    const float2* ml = p.ws_ml + row * p.n_parts;
-    const float* wo = p.ws_o + row * p.n_parts * D;
 
-    const int c4 = tid % C4;
-    const int pg = tid / C4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float den = 0.f, m = -INFINITY;
     for (int i0 = pg; i0 < np; i0 += 4 * NPG) {
-        float2 mlv[4];
-        float4 ov[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = i0 + u * NPG;
-            const int ic = i < np ? i : i0;
-            mlv[u] = ml[ic];
-            ov[u] = reinterpret_cast<const float4*>(wo + (int64_t)ic * D)[c4];
-            if (i >= np) mlv[u].x = -INFINITY;
-        }
+        if (i0 != pg) load_batch(i0);
         float mn = m;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) mn = fmaxf(mn, mlv[u].x);
+        for (int u = 0; u < 4; ++u)
+            if (i0 + u * NPG < np) mn = fmaxf(mn, mlv[u].x);
         const float a = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first batch
         acc.x *= a; acc.y *= a; acc.z *= a; acc.w *= a;
         den *= a;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const float w = __builtin_amdgcn_exp2f(mlv[u].x - mn);
-            acc.x = fmaf(w, ov[u].x, acc.x);
-            acc.y = fmaf(w, ov[u].y, acc.y);
-            acc.z = fmaf(w, ov[u].z, acc.z);
-            acc.w = fmaf(w, ov[u].w, acc.w);
-            den = fmaf(w, mlv[u].y, den);
+            if (i0 + u * NPG < np) {
+                const float w = __builtin_amdgcn_exp2f(mlv[u].x - mn);
+                acc.x = fmaf(w, ov[u].x, acc.x);
+                acc.y = fmaf(w, ov[u].y, acc.y);
+                acc.z = fmaf(w, ov[u].z, acc.z);
+                acc.w = fmaf(w, ov[u].w, acc.w);
+                den = fmaf(w, mlv[u].y, den);
+            }
         }
         m = mn;
     }

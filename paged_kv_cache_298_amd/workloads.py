@@ -78,6 +78,9 @@ class Workload:
     cow_pairs: np.ndarray          # int32 [N, 2] (src, dst) blocks to clone before writing
     logical_k: list = field(default_factory=list)   # per sequence [L, Hkv, D], if kept
     logical_v: list = field(default_factory=list)
+    # int32 [n_groups, 3] (first sequence, members, tokens whose table entries all members
+    # share), for workloads built with shared prompts; empty otherwise
+    share_groups: np.ndarray = field(default_factory=lambda: np.zeros((0, 3), np.int32))
 
     @property
     def G(self):
@@ -256,12 +259,16 @@ def make_shared_prefix(name, n_prompts, n_cand, prompt_len, div_max, Hq, Hkv, D,
                 logical_k.append(np.concatenate([kp[p], kd[b]], axis=0))
                 logical_v.append(np.concatenate([vp[p], vd[b]], axis=0))
     scale = float(np.float32(1.0 / math.sqrt(D)))
+    # the cloned last prompt block is no longer a shared table entry
+    shared_tokens = (p_blocks - 1) * bs if clone_last_prompt_block and n_cand > 1 else prompt_len
     return Workload(name=name, dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, D=D, block_size=bs,
                     num_blocks=num_blocks, max_blocks=max_blocks, scale=scale, q=q,
                     k_cache=k_cache, v_cache=v_cache, block_tables=tables, seq_lens=seq_lens,
                     new_key=new_key, new_value=new_value, slot_mapping=slots,
                     cow_pairs=np.asarray(pairs, dtype=np.int32).reshape(-1, 2),
-                    logical_k=logical_k, logical_v=logical_v)
+                    logical_k=logical_k, logical_v=logical_v,
+                    share_groups=np.asarray([(p * n_cand, n_cand, shared_tokens)
+                                             for p in range(n_prompts)], np.int32).reshape(-1, 3))
 
 
 CONFIG_NAMES = {

@@ -49,3 +49,24 @@ def test_unsorted_stays_in_range():
         for b in range(-1, 101, 7):
             got, steps = _search(firsts, b)
             assert -1 <= got < n and steps <= 3
+
+
+def test_workload_share_groups_meet_the_preconditions():
+    """The groups the shared-prompt generator reports: sorted, disjoint, and every member's
+    table entries over the shared tokens equal the first member's."""
+    from paged_kv_cache_298_amd import workloads as W
+    for wl in (W.config(3, poison=False),
+               W.make_shared_prefix("g", 3, 4, 512, 40, 32, 8, 128, 16, W.BF16, seed=2),
+               W.make_shared_prefix("g", 2, 3, 384, 20, 16, 4, 64, 32, W.BF16, seed=4)):
+        g = wl.share_groups
+        assert g.shape[1] == 3 and len(g) > 0
+        assert np.all(np.diff(g[:, 0]) >= g[:-1, 1])
+        for first, members, shared in g:
+            nb = shared // wl.block_size
+            assert shared % wl.block_size == 0 and nb > 0
+            for b in range(first, first + members):
+                assert wl.seq_lens[b] >= shared
+                assert np.array_equal(wl.block_tables[b, :nb], wl.block_tables[first, :nb])
+            # the next block is private to each member (the copy-on-write clone)
+            if members > 1:
+                assert len({int(wl.block_tables[b, nb]) for b in range(first, first + members)}) == members
