@@ -45,3 +45,29 @@ def attention(q, K, V, scale):
         scores = s64 * (K[:, g, :] @ q[h])
         out[h] = softmax(scores) @ V[:, g, :]
     return out
+
+
+def causal_attention(Q, K, V, scale):
+    """Causal softmax attention of a sequence's last n tokens, in matrix form.
+
+    Q [n, Hq, D] are the queries of positions L - n .. L - 1; K, V [L, Hkv, D] in logical
+    token order. Query j may see tokens 0 .. L - n + j: the scores above that diagonal are
+    set to -inf before the row softmax. Returns float64 [n, Hq, D].
+    """
+    Q = to_f64(Q)
+    K = to_f64(K)
+    V = to_f64(V)
+    n, Hq, D = Q.shape
+    L, Hkv, _ = K.shape
+    group = Hq // Hkv
+    out = np.zeros((n, Hq, D), dtype=np.float64)
+    if n == 0:
+        return out
+    s64 = float(np.float32(scale))
+    visible = np.arange(L)[None, :] <= (L - n + np.arange(n))[:, None]     # [n, L]
+    for h in range(Hq):
+        g = h // group
+        S = s64 * (Q[:, h, :] @ K[:, g, :].T)
+        S = np.where(visible, S, -np.inf)
+        out[:, h, :] = softmax(S, axis=1) @ V[:, g, :]
+    return out

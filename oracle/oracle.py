@@ -28,11 +28,13 @@ def _load():
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.oracle_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                       f32, i32, vp, i32, i32]
+        lib.oracle_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                            i32, i32, f32, i32, vp, i32, i32]
         lib.oracle_gather.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32]
         lib.oracle_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32]
         lib.oracle_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32]
         lib.oracle_max_threads.argtypes = []
-        for fn in (lib.oracle_decode, lib.oracle_gather, lib.oracle_reshape_and_cache,
+        for fn in (lib.oracle_decode, lib.oracle_decode_multi, lib.oracle_gather, lib.oracle_reshape_and_cache,
                    lib.oracle_copy_blocks, lib.oracle_max_threads):
             fn.restype = ctypes.c_int
         _lib = lib
@@ -93,6 +95,46 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale, rows=None, thread
                            B, Hq, Hkv, D, bs, nb, max_blocks, float(np.float32(scale)), code,
                            rp, nr, int(threads))
     _check(st, "oracle_decode")
+    return out
+
+
+def decode_multi(q, k_cache, v_cache, block_tables, seq_lens, q_starts, scale, rows=None,
+                 threads=0):
+    """Multi-query paged attention with a causal mask, in fp64.
+
+    q [total_q, Hq, D]: the last n_b = q_starts[b+1] - q_starts[b] tokens of each sequence,
+    in position order; query j of sequence b attends to tokens 0 .. seq_lens[b] - n_b + j.
+    q_starts int32 [B + 1]. rows: optional list of flat rows qi * Hq + h; then the result
+    is [len(rows), D], else [total_q, Hq, D]. Returns float64.
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q)
+    k_cache = np.ascontiguousarray(k_cache)
+    v_cache = np.ascontiguousarray(v_cache)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(q_starts, dtype=np.int32)
+    code = _dtype_code(k_cache)
+    if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("q, k_cache and v_cache must share one element type")
+    total, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    B = sl.shape[0]
+    if (D2 != D or v_cache.shape != k_cache.shape or bt.shape[0] != B or qs.shape != (B + 1,)
+            or int(qs[-1]) != total):
+        raise ValueError("shape mismatch")
+    max_blocks = bt.shape[1] if bt.ndim == 2 else 0
+    if rows is None:
+        out = np.zeros((total, Hq, D), dtype=np.float64)
+        rp, nr = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int32)
+        out = np.zeros((len(rows), D), dtype=np.float64)
+        rp, nr = _ptr(rows), len(rows)
+    st = lib.oracle_decode_multi(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt),
+                                 _ptr(sl), _ptr(qs), B, Hq, Hkv, D, bs, nb, max_blocks,
+                                 float(np.float32(scale)), code, rp, nr, int(threads))
+    _check(st, "oracle_decode_multi")
     return out
 
 

@@ -177,6 +177,93 @@ int oracle_decode(double* out, const void* q, const void* k_cache, const void* v
     return status;
 }
 
+/*
+ * Multi-query paged attention with a causal mask: several of a sequence's newest tokens
+ * attend at once. This covers the prefill phase of [P4] §1 (all prompt tokens computed in
+ * parallel), a later chunk of a long prompt, and several draft tokens checked in one
+ * pass; the decode step of [P4] §1 is the case of one query per sequence.
+ *
+ * Reading (the pages give no kernel for this phase): the chunk's keys and values are
+ * already in the cache (the cache write has stored them at their slots), and the chunk is
+ * the sequence's last n_b tokens, n_b = q_starts[b + 1] - q_starts[b] <= seq_lens[b].
+ * Query j of sequence b therefore sits at position p = seq_lens[b] - n_b + j and attends
+ * to tokens 0 .. p, its own included, exactly as a decode step at length p + 1 would.
+ *
+ * q        : [total_q, Hq, D], total_q = q_starts[B]; the rows of sequence b are
+ *            q_starts[b] .. q_starts[b + 1] - 1, in position order
+ * q_starts : int32 [B + 1], q_starts[0] = 0, non-decreasing
+ * out      : fp64, [n_rows, D] if rows != NULL (row r is rows[r] = qi * Hq + h for global
+ *            query qi), else [total_q * Hq, D]
+ * Every other argument is as for oracle_decode.
+ */
+int oracle_decode_multi(double* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* seq_lens,
+                        const int32_t* q_starts, int B, int Hq, int Hkv, int D, int bs,
+                        int num_blocks, int max_blocks, float scale, int dtype,
+                        const int32_t* rows, int n_rows, int threads) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || max_blocks < 0) return ORC_BAD_ARG;
+    if (Hq % Hkv != 0 || (dtype != 0 && dtype != 1) || q_starts[0] != 0) return ORC_BAD_ARG;
+    for (int b = 0; b < B; ++b) {
+        const int n = q_starts[b + 1] - q_starts[b];
+        if (n < 0 || seq_lens[b] < n || seq_lens[b] > max_blocks * bs) return ORC_BAD_ARG;
+    }
+    const int G = Hq / Hkv;
+    const int total = q_starts[B];
+    const int all = (rows == NULL);
+    const int nr = all ? total * Hq : n_rows;
+    int* want = (int*)malloc(sizeof(int) * (size_t)(total * Hq > 0 ? total * Hq : 1));
+    if (!want) return ORC_BAD_ARG;
+    for (int i = 0; i < total * Hq; ++i) want[i] = all ? i : -1;
+    if (!all) {
+        for (int r = 0; r < nr; ++r) {
+            if (rows[r] < 0 || rows[r] >= total * Hq) { free(want); return ORC_BAD_ARG; }
+            want[rows[r]] = r;
+        }
+    }
+    int status = ORC_OK;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int pair = 0; pair < B * Hkv; ++pair) {
+        const int b = pair / Hkv;
+        const int g = pair % Hkv;
+        const int n = q_starts[b + 1] - q_starts[b];
+        if (n == 0) continue;
+        const int L = seq_lens[b];
+        double* kc = (double*)malloc(sizeof(double) * ((size_t)L * D + 1));
+        double* vc = (double*)malloc(sizeof(double) * ((size_t)L * D + 1));
+        double* s = (double*)malloc(sizeof(double) * ((size_t)L + 1));
+        double* qrow = (double*)malloc(sizeof(double) * (size_t)D);
+        int st = (kc && vc && s && qrow) ? ORC_OK : ORC_BAD_ARG;
+        if (st == ORC_OK)
+            st = materialize(kc, vc, k_cache, v_cache, block_tables + (int64_t)b * max_blocks,
+                             L, g, Hkv, D, bs, num_blocks, dtype);
+        for (int j = 0; st == ORC_OK && j < n; ++j) {
+            const int qi = q_starts[b] + j;
+            const int p = L - n + j;           /* the query's position */
+            for (int i = 0; i < G; ++i) {
+                const int h = g * G + i;
+                const int r = want[qi * Hq + h];
+                if (r < 0) continue;
+                for (int d = 0; d < D; ++d)
+                    qrow[d] = load_elem(q, ((int64_t)qi * Hq + h) * D + d, dtype);
+                /* the causal mask: tokens 0 .. p are the first p + 1 gathered rows */
+                attend_row(out + (int64_t)r * D, qrow, kc, vc, p + 1, D, (double)scale, s);
+            }
+        }
+        if (st != ORC_OK) {
+#pragma omp critical
+            status = st;
+        }
+        free(kc); free(vc); free(s); free(qrow);
+    }
+    free(want);
+    return status;
+}
+
 /* Gather one sequence's contiguous K and V for one KV head (the materialize step on its
  * own, for round-trip tests): k_out, v_out are fp64 [L, D]. */
 int oracle_gather(double* k_out, double* v_out, const void* k_cache, const void* v_cache,

@@ -81,6 +81,8 @@ class Workload:
     # int32 [n_groups, 3] (first sequence, members, tokens whose table entries all members
     # share), for workloads built with shared prompts; empty otherwise
     share_groups: np.ndarray = field(default_factory=lambda: np.zeros((0, 3), np.int32))
+    # int32 [B + 1] query offsets of a multi-query workload (None: one query per sequence)
+    q_starts: np.ndarray = None
 
     @property
     def G(self):
@@ -93,13 +95,13 @@ class Workload:
 
 
 def _scatter_sequence(pool, table, rows, bs, skip_last):
-    """Store rows [L, Hkv, D] (logical order) into the blocks table[0:n]; the final row is
-    left out when skip_last (it is the newest token, written by the step itself)."""
+    """Store rows [L, Hkv, D] (logical order) into the blocks table[0:n]; the last
+    int(skip_last) rows are left out (the newest tokens, written by the step itself)."""
     L = rows.shape[0]
     if L == 0:
         return
     n = (L + bs - 1) // bs
-    stored = L - 1 if skip_last else L
+    stored = L - int(skip_last)
     for j in range(n):
         lo, hi = j * bs, min((j + 1) * bs, stored)
         if hi <= lo:
@@ -111,9 +113,15 @@ def _scatter_sequence(pool, table, rows, bs, skip_last):
 def make_workload(name, B, Hq, Hkv, D, block_size, seq_lens, dtype, seed, *,
                   max_blocks=None, pool_factor=1.25, num_blocks=None, placement="permute",
                   poison=True, keep_logical=False, k_row_scale_mask=None, rng=None,
-                  scale=None):
+                  scale=None, n_new=None):
     """General builder. seq_lens are given (already drawn); the placement permutation, q,
-    K and V are then drawn from rng (or default_rng(seed)) in that order."""
+    K and V are then drawn from rng (or default_rng(seed)) in that order.
+
+    n_new (multi-query workloads): per sequence, how many of its newest tokens are queries
+    at once (0 <= n_new[b] <= seq_lens[b]). Those tokens are left out of the cache and
+    handed to the step as new_key / new_value [sum n_new, Hkv, D] with their slots; q is
+    then [sum n_new, Hq, D] in position order and q_starts [B + 1] its offsets. Without
+    it, each sequence has one query and one new token (the decode step)."""
     rng = np.random.default_rng(seed) if rng is None else rng
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     bs = int(block_size)
@@ -139,7 +147,15 @@ def make_workload(name, B, Hq, Hkv, D, block_size, seq_lens, dtype, seed, *,
         tables[b, :nblk[b]] = perm[cursor:cursor + nblk[b]]
         cursor += int(nblk[b])
     sdt = _store_dtype(dtype)
-    q = _draw(rng, (B, Hq, D), dtype)
+    if n_new is not None:
+        n_new = np.asarray(n_new, dtype=np.int32)
+        if n_new.shape != (B,) or np.any(n_new < 0) or np.any(n_new > seq_lens):
+            raise ValueError("n_new must give 0 <= n_new[b] <= seq_lens[b] per sequence")
+        q_starts = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+        q = _draw(rng, (int(q_starts[-1]), Hq, D), dtype)
+    else:
+        q_starts = None
+        q = _draw(rng, (B, Hq, D), dtype)
     ks = [_draw(rng, (int(L), Hkv, D), dtype) for L in seq_lens]
     vs = [_draw(rng, (int(L), Hkv, D), dtype) for L in seq_lens]
     if k_row_scale_mask is not None:
@@ -156,17 +172,32 @@ def make_workload(name, B, Hq, Hkv, D, block_size, seq_lens, dtype, seed, *,
     fill = _fill_value(dtype, poison)
     k_cache = np.full((num_blocks, Hkv, bs, D), fill, dtype=sdt)
     v_cache = np.full((num_blocks, Hkv, bs, D), fill, dtype=sdt)
-    new_key = np.zeros((B, Hkv, D), dtype=sdt)
-    new_value = np.zeros((B, Hkv, D), dtype=sdt)
-    slots = np.full((B,), -1, dtype=np.int32)
-    for b in range(B):
-        L = int(seq_lens[b])
-        _scatter_sequence(k_cache, tables[b], ks[b], bs, skip_last=True)
-        _scatter_sequence(v_cache, tables[b], vs[b], bs, skip_last=True)
-        if L > 0:
-            new_key[b] = ks[b][L - 1]
-            new_value[b] = vs[b][L - 1]
-            slots[b] = tables[b, (L - 1) // bs] * bs + (L - 1) % bs
+    if n_new is None:
+        new_key = np.zeros((B, Hkv, D), dtype=sdt)
+        new_value = np.zeros((B, Hkv, D), dtype=sdt)
+        slots = np.full((B,), -1, dtype=np.int32)
+        for b in range(B):
+            L = int(seq_lens[b])
+            _scatter_sequence(k_cache, tables[b], ks[b], bs, skip_last=True)
+            _scatter_sequence(v_cache, tables[b], vs[b], bs, skip_last=True)
+            if L > 0:
+                new_key[b] = ks[b][L - 1]
+                new_value[b] = vs[b][L - 1]
+                slots[b] = tables[b, (L - 1) // bs] * bs + (L - 1) % bs
+    else:
+        T = int(q_starts[-1])
+        new_key = np.zeros((T, Hkv, D), dtype=sdt)
+        new_value = np.zeros((T, Hkv, D), dtype=sdt)
+        slots = np.full((T,), -1, dtype=np.int32)
+        for b in range(B):
+            L, n = int(seq_lens[b]), int(n_new[b])
+            _scatter_sequence(k_cache, tables[b], ks[b], bs, skip_last=n)
+            _scatter_sequence(v_cache, tables[b], vs[b], bs, skip_last=n)
+            for j in range(n):
+                pos, i = L - n + j, int(q_starts[b]) + j
+                new_key[i] = ks[b][pos]
+                new_value[i] = vs[b][pos]
+                slots[i] = tables[b, pos // bs] * bs + pos % bs
     if scale is None:
         scale = float(np.float32(1.0 / math.sqrt(D)))
     return Workload(name=name, dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, D=D, block_size=bs,
@@ -174,7 +205,8 @@ def make_workload(name, B, Hq, Hkv, D, block_size, seq_lens, dtype, seed, *,
                     k_cache=k_cache, v_cache=v_cache, block_tables=tables, seq_lens=seq_lens,
                     new_key=new_key, new_value=new_value, slot_mapping=slots,
                     cow_pairs=np.zeros((0, 2), dtype=np.int32),
-                    logical_k=ks if keep_logical else [], logical_v=vs if keep_logical else [])
+                    logical_k=ks if keep_logical else [], logical_v=vs if keep_logical else [],
+                    q_starts=q_starts)
 
 
 def make_shared_prefix(name, n_prompts, n_cand, prompt_len, div_max, Hq, Hkv, D, block_size,

@@ -36,6 +36,10 @@ MUTANTS = {
     "bf16 widened by 15 bits": ("<< 16;", "<< 15;"),
     "cache write to the wrong slot": ("const int64_t blk = s / bs, off = s % bs;",
                                       "const int64_t blk = s / bs, off = (s + 1) % bs;"),
+    "causal mask drops the query's own token": (
+        "attend_row(out + (int64_t)r * D, qrow, kc, vc, p + 1, D, (double)scale, s);",
+        "attend_row(out + (int64_t)r * D, qrow, kc, vc, p, D, (double)scale, s);"),
+    "chunk positions counted from zero": ("const int p = L - n + j;", "const int p = j;"),
     "copy moves only the first head": (
         "const size_t block_bytes = (size_t)Hkv * bs * D * (size_t)elt_bytes;",
         "const size_t block_bytes = (size_t)Hkv * bs * D * (size_t)elt_bytes;\n    const size_t copy_bytes = block_bytes / (size_t)Hkv;"),
@@ -78,7 +82,22 @@ def _check_copy(orc):
     return np.array_equal(k2[5], kc[1]) and np.array_equal(v2[5], kc[1] + 1)
 
 
-CHECKS = [_check_bruteforce, _check_copy]
+def _check_multi(orc):
+    wl = W.make_workload("mq", 3, 8, 2, 64, 16, [5, 16, 40], W.BF16, seed=23,
+                         keep_logical=True, n_new=[5, 3, 17])
+    kc, vc = orc.reshape_and_cache(wl.k_cache, wl.v_cache, wl.new_key, wl.new_value,
+                                   wl.slot_mapping)
+    got = orc.decode_multi(wl.q, kc, vc, wl.block_tables, wl.seq_lens, wl.q_starts, wl.scale)
+    qs = wl.q_starts
+    for b in range(3):
+        ref = bruteforce.causal_attention(wl.q[qs[b]:qs[b + 1]], wl.logical_k[b],
+                                          wl.logical_v[b], wl.scale)
+        if not np.max(np.abs(got[qs[b]:qs[b + 1]] - ref)) <= 1e-12:
+            return False
+    return True
+
+
+CHECKS = [_check_bruteforce, _check_copy, _check_multi]
 
 
 def _apply(name):

@@ -349,3 +349,73 @@ def test_out_of_pool_table_entry_is_rejected(oracle):
     bt[0, 1] = wl.num_blocks
     with pytest.raises(ValueError):
         oracle.decode(wl.q, wl.k_cache, wl.v_cache, bt, wl.seq_lens, wl.scale)
+
+
+# ------------------------------------------------------------------ multi-query (causal)
+
+def _multi_step(oracle, wl):
+    """Write the chunk's K/V, then the causal multi-query oracle."""
+    kc, vc = oracle.reshape_and_cache(wl.k_cache, wl.v_cache, wl.new_key, wl.new_value,
+                                      wl.slot_mapping)
+    return oracle.decode_multi(wl.q, kc, vc, wl.block_tables, wl.seq_lens, wl.q_starts,
+                               wl.scale), kc, vc
+
+
+@pytest.mark.parametrize("B, Hq, Hkv, D, bs, dtype, lens, n_new", [
+    (3, 8, 2, 64, 16, W.BF16, [5, 16, 40], [5, 3, 17]),     # whole prompt, short chunk, crossing blocks
+    (2, 6, 3, 64, 32, W.F32, [9, 48], [1, 48]),
+    (4, 4, 1, 64, 16, W.BF16, [20, 7, 33, 1], [0, 7, 2, 1]),  # a sequence with no queries
+])
+def test_multi_matches_causal_bruteforce(oracle, B, Hq, Hkv, D, bs, dtype, lens, n_new):
+    wl = W.make_workload("mq", B, Hq, Hkv, D, bs, lens, dtype, seed=23, keep_logical=True,
+                         n_new=n_new)
+    got, _, _ = _multi_step(oracle, wl)
+    qs = wl.q_starts
+    for b in range(B):
+        ref = bruteforce.causal_attention(wl.q[qs[b]:qs[b + 1]], wl.logical_k[b],
+                                          wl.logical_v[b], wl.scale)
+        assert np.max(np.abs(got[qs[b]:qs[b + 1]] - ref), initial=0.0) <= 1e-12
+
+
+def test_multi_first_prompt_token_returns_its_value_exactly(oracle):
+    """A whole prompt as queries: the query at position 0 sees only token 0."""
+    wl = W.make_workload("mq0", 2, 4, 2, 64, 16, [1, 20], W.F32, seed=3, keep_logical=True,
+                         n_new=[1, 20])
+    got, _, _ = _multi_step(oracle, wl)
+    for b, row in ((0, 0), (1, 1)):
+        for h in range(4):
+            assert np.array_equal(got[row, h], wl.logical_v[b][0, h // 2].astype(np.float64))
+
+
+def test_multi_one_query_per_sequence_is_decode(oracle):
+    lens = [1, 7, 16, 33, 50]
+    wl = W.make_workload("mq1", 5, 8, 2, 64, 16, lens, W.BF16, seed=8, n_new=[1] * 5)
+    got, kc, vc = _multi_step(oracle, wl)
+    dec = oracle.decode(wl.q, kc, vc, wl.block_tables, wl.seq_lens, wl.scale)
+    assert np.array_equal(got, dec)
+
+
+def test_multi_prompt_row_equals_decode_of_its_prefix(oracle):
+    """Query j of a whole prompt equals a decode step of the first j + 1 tokens."""
+    L = 37
+    wl = W.make_workload("mqp", 1, 4, 2, 64, 16, [L], W.BF16, seed=12, n_new=[L])
+    got, kc, vc = _multi_step(oracle, wl)
+    for j in (0, 5, 15, 16, 36):
+        dec = oracle.decode(wl.q[j:j + 1], kc, vc, wl.block_tables, np.array([j + 1], np.int32),
+                            wl.scale)
+        assert np.array_equal(got[j], dec[0])
+
+
+def test_multi_rows_subset_and_bad_chunks(oracle):
+    wl = W.make_workload("mqr", 3, 8, 2, 64, 16, [12, 30, 5], W.BF16, seed=2, n_new=[4, 9, 5])
+    full, kc, vc = _multi_step(oracle, wl)
+    rows = np.array([0, 13, 8 * 17 + 7, 8 * 4 + 2], np.int32)
+    sub = oracle.decode_multi(wl.q, kc, vc, wl.block_tables, wl.seq_lens, wl.q_starts,
+                              wl.scale, rows=rows)
+    assert np.array_equal(sub, full.reshape(-1, 64)[rows])
+    bad = wl.q_starts.copy()
+    bad[1] = 13                       # 13 queries for a 12-token sequence
+    bad[2:] += 9
+    with pytest.raises(ValueError):
+        oracle.decode_multi(np.zeros((int(bad[-1]), 8, 64), np.uint16), kc, vc,
+                            wl.block_tables, wl.seq_lens, bad, wl.scale)
