@@ -165,6 +165,43 @@ int32_t pa_decode_shared(float* out, const void* q, const void* k_cache, const v
 size_t pa_decode_shared_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t block_size,
                                         int32_t max_blocks, int32_t max_shared_tokens);
 
+/*
+ * pa_decode_multi -- several of each sequence's newest tokens attend at once, with a
+ * causal mask: the prompt of the prefill phase ([P4] section 1: all prompt tokens in
+ * parallel), a later chunk of a long prompt, or draft tokens checked in one pass. The
+ * decode step of pa_decode is the case of one query per sequence.
+ *
+ * The chunk's keys and values must already be in the cache (pa_reshape_and_cache at
+ * their slots). Sequence b's queries are the last n_b = q_starts[b+1] - q_starts[b] of
+ * its seq_lens[b] tokens, in position order: query j (global row q_starts[b] + j) sits at
+ * position p = seq_lens[b] - n_b + j and attends to tokens 0 .. p, its own included.
+ *
+ *   out        device fp32 [total_q, Hq, D], written
+ *   q          device [total_q, Hq, D], the cache's element type
+ *   q_starts   device int32 [B + 1]: q_starts[0] = 0, non-decreasing, q_starts[B] = total_q,
+ *              0 <= n_b <= min(seq_lens[b], max_q)
+ *   total_q    host count of query tokens
+ *   max_q      host bound on any n_b (it sizes the query tiles)
+ *   workspace  pa_decode_multi_workspace_bytes(...) bytes, 256-byte aligned, needs no
+ *              initialisation; may be NULL when that size is 0 (no token split)
+ * bf16 caches, block_size in {16, 32, 64, 128}, head_dim in {64, 128}, any Hq / Hkv;
+ * every other argument as for pa_decode. Offsets that break the preconditions are clamped
+ * on the device: wrong rows for the sequences concerned, never an access outside the
+ * buffers. Rows of queries no sequence owns are left unwritten.
+ */
+int32_t pa_decode_multi(float* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* seq_lens,
+                        const int32_t* q_starts, int32_t B, int32_t total_q, int32_t max_q,
+                        int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                        int32_t max_blocks, float scale, int32_t kv_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pa_decode_multi needs: 0 when it does not split any query's tokens
+ * (or for sizes it would reject). */
+size_t pa_decode_multi_workspace_bytes(int32_t B, int32_t total_q, int32_t max_q, int32_t Hq,
+                                       int32_t Hkv, int32_t D, int32_t block_size,
+                                       int32_t max_blocks);
+
 /* ------------------------------------------------------------------ cache write */
 
 /*

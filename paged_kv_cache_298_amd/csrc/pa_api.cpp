@@ -1,6 +1,7 @@
 // pa_api.cpp -- the C ABI declared in include/pa.h: argument validation (pure host code,
 // run before any HIP call), launch configuration, workspace sizing and status reporting.
 // Kernels are enqueued through the launchers in pa_decode.hip and pa_cache.hip.
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -99,6 +100,69 @@ int32_t choose_path(int32_t kv_dtype, int32_t B, int32_t Hkv, int32_t block_size
     if (g_path == PA_PATH_PARTITION) return pa_internal::kPathPartition;
     if (g_path == PA_PATH_STREAM) return ok ? pa_internal::kPathStream : 0;
     return ok ? pa_internal::kPathStream : pa_internal::kPathPartition;
+}
+
+}  // namespace
+
+namespace pa_internal {
+
+MultiPlan multi_plan(int32_t B, int32_t max_q, int32_t Hq, int32_t Hkv, int32_t capacity) {
+    MultiPlan m;
+    const int64_t rows = (int64_t)max_q * (Hq / Hkv);
+    m.nset = rows > 32 ? 4 : (rows > 16 ? 2 : 1);
+    m.n_tiles = (int32_t)std::max<int64_t>(1, (rows + 16 * m.nset - 1) / (16 * m.nset));
+    int64_t P = std::max<int64_t>(16, ((int64_t)capacity + 15) / 16 * 16);
+    const int64_t units = (int64_t)B * Hkv * m.n_tiles;
+    while (P > kMultiMinPart && units * ((capacity + P - 1) / P) < kMultiMinWaves)
+        P = std::max<int64_t>(kMultiMinPart, (P / 2 + 15) / 16 * 16);
+    m.part_tokens = (int32_t)P;
+    m.n_parts = (int32_t)std::max<int64_t>(1, (capacity + P - 1) / P);
+    return m;
+}
+
+}  // namespace pa_internal
+
+namespace {
+
+struct MultiWs {
+    pa_internal::MultiPlan plan;
+    size_t ml, total;
+};
+
+MultiWs multi_workspace(int32_t B, int32_t total_q, int32_t max_q, int32_t Hq, int32_t Hkv,
+                        int32_t D, int32_t block_size, int32_t max_blocks) {
+    MultiWs w;
+    w.plan = pa_internal::multi_plan(B, max_q, Hq, Hkv, block_size * max_blocks);
+    w.ml = w.total = 0;
+    if (w.plan.n_parts > 1) {
+        const size_t rows = (size_t)total_q * (size_t)Hq * (size_t)w.plan.n_parts;
+        w.ml = (rows * (size_t)D * sizeof(float) + 255) / 256 * 256;
+        w.total = w.ml + rows * 2 * sizeof(float);
+    }
+    return w;
+}
+
+}  // namespace
+
+namespace {
+
+struct SharedWs {
+    int32_t n_pre, n_suf, n_slots, P;
+    size_t ml, total;
+};
+
+SharedWs shared_workspace(int32_t B, int32_t Hq, int32_t D, int32_t block_size, int32_t max_blocks,
+                          int32_t max_shared_tokens) {
+    SharedWs w;
+    w.P = partition_tokens(block_size, max_blocks);
+    const int64_t cap = (int64_t)block_size * max_blocks;
+    w.n_pre = (int32_t)((max_shared_tokens + pa_internal::kPrefixTokens - 1) / pa_internal::kPrefixTokens);
+    w.n_suf = (int32_t)((cap + w.P - 1) / w.P);
+    w.n_slots = w.n_pre + w.n_suf;
+    const size_t rows = (size_t)B * (size_t)Hq * (size_t)w.n_slots;
+    w.ml = (rows * (size_t)D * sizeof(float) + 255) / 256 * 256;
+    w.total = w.ml + rows * 2 * sizeof(float);
+    return w;
 }
 
 }  // namespace
@@ -254,28 +318,6 @@ int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_
     return ok();
 }
 
-namespace {
-
-struct SharedWs {
-    int32_t n_pre, n_suf, n_slots, P;
-    size_t ml, total;
-};
-
-SharedWs shared_workspace(int32_t B, int32_t Hq, int32_t D, int32_t block_size, int32_t max_blocks,
-                          int32_t max_shared_tokens) {
-    SharedWs w;
-    w.P = partition_tokens(block_size, max_blocks);
-    const int64_t cap = (int64_t)block_size * max_blocks;
-    w.n_pre = (int32_t)((max_shared_tokens + pa_internal::kPrefixTokens - 1) / pa_internal::kPrefixTokens);
-    w.n_suf = (int32_t)((cap + w.P - 1) / w.P);
-    w.n_slots = w.n_pre + w.n_suf;
-    const size_t rows = (size_t)B * (size_t)Hq * (size_t)w.n_slots;
-    w.ml = (rows * (size_t)D * sizeof(float) + 255) / 256 * 256;
-    w.total = w.ml + rows * 2 * sizeof(float);
-    return w;
-}
-
-}  // namespace
 
 size_t pa_decode_shared_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t block_size,
                                         int32_t max_blocks, int32_t max_shared_tokens) {
@@ -368,6 +410,95 @@ int32_t pa_decode_shared(float* out, const void* q, const void* k_cache, const v
     const char* err = "";
     const int e = pa_internal::launch_decode_shared(a, &err);
     if (e != 0) return fail(PA_ERR_HIP, "pa_decode_shared: launch failed: %s (%d)", err, e);
+    return ok();
+}
+
+
+
+size_t pa_decode_multi_workspace_bytes(int32_t B, int32_t total_q, int32_t max_q, int32_t Hq,
+                                       int32_t Hkv, int32_t D, int32_t block_size,
+                                       int32_t max_blocks) {
+    if (B <= 0 || total_q <= 0 || max_q <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 ||
+        block_size <= 0 || max_blocks <= 0 || (int64_t)block_size * max_blocks > (int64_t)1 << 30)
+        return 0;
+    return multi_workspace(B, total_q, max_q, Hq, Hkv, D, block_size, max_blocks).total;
+}
+
+int32_t pa_decode_multi(float* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* seq_lens,
+                        const int32_t* q_starts, int32_t B, int32_t total_q, int32_t max_q,
+                        int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                        int32_t max_blocks, float scale, int32_t kv_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    if (B < 0 || total_q < 0 || max_q < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || block_size <= 0 ||
+        num_blocks <= 0 || max_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG,
+                    "pa_decode_multi: bad sizes B=%d total_q=%d max_q=%d Hq=%d Hkv=%d D=%d "
+                    "block_size=%d num_blocks=%d max_blocks=%d",
+                    B, total_q, max_q, Hq, Hkv, D, block_size, num_blocks, max_blocks);
+    if (Hq % Hkv != 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_multi: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (elt_bytes(kv_dtype) == 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_multi: kv_dtype %d is neither PA_F32 nor PA_BF16", kv_dtype);
+    if (kv_dtype != PA_BF16)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_multi: only bf16 caches are built");
+    if ((int64_t)block_size * max_blocks > (int64_t)1 << 30)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_multi: max_blocks * block_size exceeds 2^30");
+    if (total_q > 0 && max_q == 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_multi: max_q is 0 with %d queries", total_q);
+    if (D != 64 && D != 128)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_multi: head_dim %d not built (64, 128)", D);
+    if (block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_multi: block_size %d not built (16, 32, 64, 128)", block_size);
+    if (B == 0 || total_q == 0) return ok();
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !q_starts)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_multi: null pointer argument");
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(q_starts, 4))
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_multi: misaligned pointer");
+    const MultiWs mw = multi_workspace(B, total_q, max_q, Hq, Hkv, D, block_size, max_blocks);
+    const pa_internal::MultiPlan& pl = mw.plan;
+    const int64_t items = (int64_t)Hkv * pl.n_tiles * pl.n_parts * B;
+    if (items > 0x7fffffff)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_multi: work items exceed the grid limit");
+    if (pl.n_parts > 1 && (total_q > 65535 || Hq > 65535))
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_multi: %d queries of a split launch exceed 65535", total_q);
+    if (mw.total > 0) {
+        if (!workspace || workspace_bytes < mw.total)
+            return fail(PA_ERR_INVALID_ARG, "pa_decode_multi: workspace of %zu bytes needed, %zu given",
+                        mw.total, workspace ? workspace_bytes : (size_t)0);
+        if (!aligned(workspace, 256))
+            return fail(PA_ERR_INVALID_ARG, "pa_decode_multi: workspace must be 256-byte aligned");
+    }
+
+    pa_internal::MultiLaunch a;
+    a.out = out;
+    a.ws_o = mw.total > 0 ? static_cast<float*>(workspace) : nullptr;
+    a.ws_ml = mw.total > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + mw.ml) : nullptr;
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.tables = block_tables;
+    a.lens = seq_lens;
+    a.q_starts = q_starts;
+    a.B = B;
+    a.total_q = total_q;
+    a.max_q = max_q;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.bs = block_size;
+    a.num_blocks = num_blocks;
+    a.max_blocks = max_blocks;
+    a.nset = pl.nset;
+    a.n_tiles = pl.n_tiles;
+    a.part_tokens = pl.part_tokens;
+    a.n_parts = pl.n_parts;
+    a.scale = scale;
+    a.stream = stream;
+    const char* err = "";
+    const int e = pa_internal::launch_decode_multi(a, &err);
+    if (e != 0) return fail(PA_ERR_HIP, "pa_decode_multi: launch failed: %s (%d)", err, e);
     return ok();
 }
 

@@ -104,6 +104,11 @@ struct Params {
     int pre_items;           // prefix items (group, KV head, partition) of a fused launch
     int pre_blocks;          // blocks holding them, four items each
     int suf_items;           // suffix partitions of a fused launch
+    // multi-query mode only (q_starts == nullptr otherwise)
+    const int32_t* q_starts; // [B + 1] offsets of each sequence's queries in q
+    int total_q;             // query tokens in q (host value the device offsets are clamped to)
+    int max_q;               // host bound on queries per sequence
+    int n_tiles;             // query tiles per (sequence, KV head)
 };
 
 // Shared-prefix mode: the tokens sequence b shares with its group (groups are sorted by
@@ -141,6 +146,42 @@ __device__ __forceinline__ int group_shared(const Params& p, int b) {
     if (found < 0 || b < first || b - first >= members) return 0;
     sh = (sh > p.max_shared ? p.max_shared : sh) & ~15;   // whole 16-token groups only
     return sh < 0 ? 0 : sh;
+}
+
+// Multi-query mode: the first query row qs of sequence b and its query count n, clamped
+// so that 0 <= n <= min(L, max_q) and qs + n <= total_q (offsets that break the
+// preconditions give wrong rows, never an access outside q or out).
+__device__ __forceinline__ void multi_rows(const Params& p, int b, int L, int* qs, int* n) {
+    int s = p.q_starts[b];
+    const int e = p.q_starts[b + 1];
+    s = s < 0 ? 0 : (s > p.total_q ? p.total_q : s);
+    int k = e - s;
+    k = k < 0 ? 0 : k;
+    k = min(k, min(L, p.max_q));
+    k = min(k, p.total_q - s);
+    *qs = s;
+    *n = k;
+}
+
+// Multi-query mode: the sequence whose queries include global query qi, i.e. the last b
+// with q_starts[b] <= qi (0 if none). All 64 lanes of a wave call it with the same qi;
+// the same 64-way search as group_shared.
+__device__ __forceinline__ int seq_of_query(const Params& p, int qi) {
+    const int lane = threadIdx.x & 63;
+    int lo = 0, n = p.B, found = 0;
+    while (n > 0) {
+        const int stride = (n + 63) >> 6;
+        const bool in = lane * stride < n;
+        const int f = p.q_starts[lo + (in ? lane * stride : 0)];
+        const uint64_t m = __ballot(in && f <= qi);
+        if (m == 0) break;
+        found = lo + (63 - __builtin_clzll(m)) * stride;
+        if (stride == 1) break;
+        const int end = lo + n;
+        lo = found + 1;
+        n = min(stride - 1, end - lo);
+    }
+    return found;
 }
 
 __device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u << 16); }
@@ -1110,6 +1151,295 @@ __device__ __forceinline__ void prefix_item(const Params& p, int id) {
     }
 }
 
+// Multi-query attention with a causal mask (prefill, a chunk of a long prompt, draft
+// tokens): the last n_b tokens of sequence b are queries at once, query j at position
+// p_j = L_b - n_b + j seeing tokens 0 .. p_j. One wavefront per (KV head, query tile,
+// token partition, sequence). A query tile is 16 NSET of the sequence's n_b x G query rows
+// (row = j G + head, so consecutive rows of a token share its position); they are the
+// columns of the score tiles as in prefix_item, so each K and V tile read serves the whole
+// tile. The partition covers tokens [part P, (part + 1) P) up to the tile's last position;
+// a group that reaches past the tile's first position is masked per column (a select, so
+// poison never leaks). The table entries of 64 groups at a time sit in one VGPR.
+// A row whose position lies in partition 0 (np = 1) is written normalized; otherwise
+// every partition leaves a record and multi rows are merged by decode_reduce_kernel.
+template <int D, int NSET>
+__device__ __forceinline__ void multi_item(const Params& p, int id) {
+    constexpr int ROW = D * 2;
+    constexpr int NQ = D / 32;
+    constexpr int WV = D / 8;
+    constexpr int EV = D / 16;
+    constexpr int DEPTH = 4;             // ring items: K and V of two groups
+    constexpr int U = DEPTH / 2;
+    static_assert(D == 64 || D == 128, "head size");
+
+    const int lane = threadIdx.x & 63;
+    const int g = id % p.Hkv;
+    int rest = id / p.Hkv;
+    const int tile = rest % p.n_tiles;
+    rest /= p.n_tiles;
+    const int part = rest % p.n_parts;
+    const int b = rest / p.n_parts;
+    if (b >= p.B) return;
+    const int cap = p.max_blocks * p.bs;
+    int L = p.lens[b];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    int qs, n;
+    multi_rows(p, b, L, &qs, &n);
+    const int G = p.Hq / p.Hkv;
+    const int row0 = tile * 16 * NSET;
+    const int M = min(16 * NSET, n * G - row0);   // query rows of this tile
+    if (M <= 0) return;
+    const int base = L - n;                        // position of the chunk's first query
+    const int pos_first = base + row0 / G;
+    const int pos_last = base + (row0 + M - 1) / G;
+    const int P = p.part_tokens;
+    const int t0 = part * P;
+    if (t0 > pos_last) return;
+    const int ntok = min(pos_last + 1, t0 + P) - t0;
+    const int ng = (ntok + 15) >> 4;
+    const int last = ng - 1;
+
+    // table entries of groups 64w .. 64w + 63 of the partition, lane i holding group 64w + i
+    const int32_t* trow = p.tables + (int64_t)b * p.max_blocks;
+    auto load_window = [&](int w) -> int {
+        int i = (t0 + (w * 64 + lane) * 16) >> p.bs_shift;
+        i = i < p.max_blocks ? i : p.max_blocks - 1;
+        const int e = trow[i];
+        return e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);
+    };
+    int tblv = load_window(0);
+    int win = 0;
+
+    const int r = lane >> 4;
+    const int c = lane & 15;
+    u32x4_t qf[NSET][NQ];
+    int pos_c[NSET];                     // position of column c of set s (-1 past the tile)
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+        const int qr = 16 * s + c;
+        if (qr < M) {
+            const int row = row0 + qr;
+            const int j = row / G, hh = row - j * G;
+            pos_c[s] = base + j;
+            const char* qrow = p.q + ((int64_t)(qs + j) * p.Hq + g * G + hh) * ROW;
+#pragma unroll
+            for (int k = 0; k < NQ; ++k)
+                qf[s][k] = *reinterpret_cast<const u32x4_t*>(qrow + (k * 32 + r * 8) * 2);
+        } else {
+            pos_c[s] = -1;
+#pragma unroll
+            for (int k = 0; k < NQ; ++k) qf[s][k] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+
+    const int64_t tile_bytes = (int64_t)p.bs * ROW;
+    const int64_t blk_bytes = (int64_t)p.Hkv * tile_bytes;
+    const int bs_mask = p.bs - 1;
+    const char* kbase = p.k + g * tile_bytes;
+    const char* vbase = p.v + g * tile_bytes;
+    const uint32_t koff = (uint32_t)(((c >> 2) + 4 * (c & 3)) * ROW + r * 16);
+    const uint32_t voff = (uint32_t)(r * ROW + c * WV);
+    struct Item {
+        u32x4_t q[NQ];
+    };
+    auto goff = [&](int gq) -> int64_t {
+        gq = gq < last ? gq : last;
+        const int w = gq >> 6;
+        if (w != win) {
+            // a new window of table entries (every 64 groups): the ring drains once
+            win = w;
+            tblv = load_window(w);
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        }
+        const int ph = __builtin_amdgcn_readlane(tblv, gq & 63);
+        return (int64_t)ph * blk_bytes + (int64_t)((t0 + gq * 16) & bs_mask) * ROW;
+    };
+    auto issue_k = [&](int gq, Item& dst) {
+        const char* kb = kbase + goff(gq);
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) dst.q[k] = *reinterpret_cast<const u32x4_t*>(kb + koff + k * 64);
+    };
+    auto issue_v = [&](int gq, Item& dst) {
+        const char* vb = vbase + goff(gq);
+        if constexpr (WV == 16) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                dst.q[k] = *reinterpret_cast<const u32x4_t*>(vb + voff + k * 4 * ROW);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; k += 2) {
+                const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vb + voff + k * 4 * ROW);
+                const u32x2_t e = *reinterpret_cast<const u32x2_t*>(vb + voff + (k + 1) * 4 * ROW);
+                dst.q[k / 2] = __builtin_shufflevector(a, e, 0, 1, 2, 3);
+            }
+        }
+    };
+    auto vword = [&](const Item& it, int k, int w) -> uint32_t {
+        if constexpr (WV == 16) return it.q[k][w];
+        else return it.q[k >> 1][(k & 1) * 2 + w];
+    };
+
+    f32x4_t acc[NSET][EV];
+    float m_run[NSET], l_run[NSET];
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+        m_run[s] = -INFINITY;
+        l_run[s] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) acc[s][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const float cl2 = p.scale_log2;
+    Item ring[DEPTH];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_k(u, ring[2 * u]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_v(u, ring[2 * u + 1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int t0g = 0; t0g < ng; t0g += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = t0g + u;
+            Item& kit = ring[2 * u];
+            Item& vit = ring[2 * u + 1];
+            const bool live = t < ng;
+            const int valid = min(16, ntok - 16 * t);
+            const int tg = t0 + 16 * t;          // first token of the group
+            float y[NSET][4];
+            uint32_t pw[NSET][2];
+            if (live) {
+#pragma unroll
+                for (int s = 0; s < NSET; ++s) {
+                    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int k = 0; k < NQ; ++k)
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, kit.q[k]),
+                            __builtin_bit_cast(bf16x8_t, qf[s][k]), sc, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y[s][i] = sc[i] * cl2;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            issue_k(t + U, kit);
+            __builtin_amdgcn_sched_barrier(0);
+            if (live) {
+                // the causal edge (and the partition's end) fall inside this group
+                const bool edge = tg + 15 > pos_first;
+#pragma unroll
+                for (int s = 0; s < NSET; ++s) {
+                    if (edge) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) y[s][i] = (tg + r + 4 * i <= pos_c[s]) ? y[s][i] : -INFINITY;
+                    }
+                    const float mx = fmaxf(fmaxf(y[s][0], y[s][1]), fmaxf(y[s][2], y[s][3]));
+                    const float m_new = fmaxf(m_run[s], rows_max(mx));
+                    // a column that has seen no token yet keeps m = -inf: use 0 as its
+                    // reference so that its factors are exactly 0 instead of NaN
+                    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_ref);   // per column
+                    m_run[s] = m_new;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float ai = __shfl(alpha, 4 * r + i);
+#pragma unroll
+                        for (int e = 0; e < EV; ++e) acc[s][e][i] *= ai;
+                    }
+                    const bf16x2_t p01 = __builtin_convertvector(
+                        (f32x2_t){__builtin_amdgcn_exp2f(y[s][0] - m_ref), __builtin_amdgcn_exp2f(y[s][1] - m_ref)}, bf16x2_t);
+                    const bf16x2_t p23 = __builtin_convertvector(
+                        (f32x2_t){__builtin_amdgcn_exp2f(y[s][2] - m_ref), __builtin_amdgcn_exp2f(y[s][3] - m_ref)}, bf16x2_t);
+                    pw[s][0] = __builtin_bit_cast(uint32_t, p01);
+                    pw[s][1] = __builtin_bit_cast(uint32_t, p23);
+                    l_run[s] = l_run[s] * alpha + ((lo_bf16(pw[s][0]) + hi_bf16(pw[s][0])) +
+                                                   (lo_bf16(pw[s][1]) + hi_bf16(pw[s][1])));
+                }
+                if (valid < 16) {
+                    // rows past the partition's last token may hold anything (the tail of
+                    // the sequence's last block): their probabilities are 0, their values too
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        if (r + 4 * k >= valid) {
+                            if constexpr (WV == 16) {
+                                vit.q[k] = u32x4_t{0u, 0u, 0u, 0u};
+                            } else {
+                                vit.q[k >> 1][(k & 1) * 2] = 0u;
+                                vit.q[k >> 1][(k & 1) * 2 + 1] = 0u;
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int w = 0; w < WV / 4; ++w) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+                        const u32x2_t bv = {__builtin_amdgcn_perm(vword(vit, 1, w), vword(vit, 0, w), sel),
+                                            __builtin_amdgcn_perm(vword(vit, 3, w), vword(vit, 2, w), sel)};
+#pragma unroll
+                        for (int s = 0; s < NSET; ++s) {
+                            const u32x2_t av = {pw[s][0], pw[s][1]};
+                            acc[s][2 * w + h] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                                __builtin_bit_cast(s16x4_t, av), __builtin_bit_cast(s16x4_t, bv),
+                                acc[s][2 * w + h], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            issue_v(t + U, vit);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // output row qr = 16 s + 4 r + i sits in lane (r, c), columns c*EV..; its (max, sum)
+    // were kept per column qr
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+        const float lcol = rows_sum(l_run[s]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int qr = 16 * s + 4 * r + i;
+            const float lr = __shfl(lcol, 4 * r + i);
+            const float mr = __shfl(m_run[s], 4 * r + i);
+            if (qr < M) {
+                const int row = row0 + qr;
+                const int j = row / G, hh = row - j * G;
+                const int pos = base + j;
+                if (pos >= t0) {
+                    const int64_t grow = (int64_t)(qs + j) * p.Hq + g * G + hh;
+                    if (pos < P) {                  // the row's only partition
+                        const float inv = 1.0f / lr;
+                        float* dst = p.out + grow * D + c * EV;
+#pragma unroll
+                        for (int e = 0; e < EV; e += 4)
+                            *reinterpret_cast<float4*>(dst + e) =
+                                make_float4(acc[s][e][i] * inv, acc[s][e + 1][i] * inv,
+                                            acc[s][e + 2][i] * inv, acc[s][e + 3][i] * inv);
+                    } else {
+                        float* dst = p.ws_o + (grow * p.n_parts + part) * D + c * EV;
+#pragma unroll
+                        for (int e = 0; e < EV; e += 4)
+                            *reinterpret_cast<float4*>(dst + e) =
+                                make_float4(acc[s][e][i], acc[s][e + 1][i], acc[s][e + 2][i], acc[s][e + 3][i]);
+                        if (c == 0) p.ws_ml[grow * p.n_parts + part] = make_float2(mr, lr);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// All multi-query items, four per 256-thread block.
+template <int D, int NSET>
+__global__ __launch_bounds__(256) void decode_multi_kernel(Params p) {
+    const int item = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (item < p.pre_items) multi_item<D, NSET>(p, item);
+}
+
 // The prefix partitions and the members' own tokens in one launch of 4-wave blocks, one
 // item per wave: blocks below pre_blocks hold the prefix items (first, so that the longest
 // work starts earliest), the rest the suffix partitions. A suffix partition is short (the
@@ -1142,11 +1472,11 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
     __shared__ float2 red_ml[NPG];
 
     const int h = blockIdx.x;
-    const int b = blockIdx.y;
+    const int y = blockIdx.y;          // the sequence, or in multi-query mode the query
     const int tid = threadIdx.x;
     const int c4 = tid % C4;
     const int pg = tid / C4;
-    const int64_t row = (int64_t)b * p.Hq + h;
+    const int64_t row = (int64_t)y * p.Hq + h;
     const float2* ml = p.ws_ml + row * p.n_parts;
     const float* wo = p.ws_o + row * p.n_parts * D;
     float2 mlv[4];
@@ -1162,27 +1492,41 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
     };
     load_batch(pg);
 
-    // the length through a vector load (b copied into a VGPR) that the group search's
-    // loads follow without a wait: a scalar load would be waited for first
-    int bv;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(bv) : "s"(b));
-    const int L_raw = p.lens[bv];
-    const int sh = p.groups != nullptr ? group_shared(p, b) : 0;
     const int cap = p.max_blocks * p.bs;
-    const int L = L_raw < 0 ? 0 : (L_raw > cap ? cap : L_raw);
     int np;
-    if (p.groups != nullptr) {
-        // shared-prefix mode: the prefix partitions of b's group, then b's own partitions,
-        // all left as records (an empty sequence gets a zero row here)
-        const int start = min(sh, L);
-        np = (start + p.pre_tokens - 1) / p.pre_tokens + (L - start + p.part_tokens - 1) / p.part_tokens;
-        if (np == 0) {
-            for (int i = tid; i < D; i += 256) p.out[row * D + i] = 0.f;
-            return;
-        }
-    } else {
-        np = (L + p.part_tokens - 1) / p.part_tokens;
+    if (p.q_starts != nullptr) {
+        // multi-query mode: query y of sequence b at position pos has pos / P + 1 partitions
+        const int b = seq_of_query(p, y);
+        int L = p.lens[b];
+        L = L < 0 ? 0 : (L > cap ? cap : L);
+        int qs, n;
+        multi_rows(p, b, L, &qs, &n);
+        const int j = y - qs;
+        if (j < 0 || j >= n) return;
+        np = (L - n + j) / p.part_tokens + 1;
         if (np <= 1) return;
+    } else {
+        const int b = y;
+        // the length through a vector load (b copied into a VGPR) that the group search's
+        // loads follow without a wait: a scalar load would be waited for first
+        int bv;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(bv) : "s"(b));
+        const int L_raw = p.lens[bv];
+        const int sh = p.groups != nullptr ? group_shared(p, b) : 0;
+        const int L = L_raw < 0 ? 0 : (L_raw > cap ? cap : L_raw);
+        if (p.groups != nullptr) {
+            // shared-prefix mode: the prefix partitions of b's group, then b's own partitions,
+            // all left as records (an empty sequence gets a zero row here)
+            const int start = min(sh, L);
+            np = (start + p.pre_tokens - 1) / p.pre_tokens + (L - start + p.part_tokens - 1) / p.part_tokens;
+            if (np == 0) {
+                for (int i = tid; i < D; i += 256) p.out[row * D + i] = 0.f;
+                return;
+            }
+        } else {
+            np = (L + p.part_tokens - 1) / p.part_tokens;
+            if (np <= 1) return;
+        }
     }
 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1880,6 +2224,17 @@ hipError_t launch_shared_d(Params prm, int G, int nset, int n_pre, int n_suf, vo
     return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_multi_d(const Params& prm, int nset, hipStream_t s) {
+    const dim3 grid((prm.pre_items + 3) / 4);
+    if (nset == 1) hipLaunchKernelGGL((decode_multi_kernel<D, 1>), grid, dim3(256), 0, s, prm);
+    else if (nset == 2) hipLaunchKernelGGL((decode_multi_kernel<D, 2>), grid, dim3(256), 0, s, prm);
+    else hipLaunchKernelGGL((decode_multi_kernel<D, 4>), grid, dim3(256), 0, s, prm);
+    if (prm.n_parts > 1)
+        hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(prm.Hq, prm.total_q), dim3(256), 0, s, prm);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 namespace pa_internal {
@@ -1967,6 +2322,45 @@ int launch_decode_shared(const SharedLaunch& a, const char** err) {
     const int nset = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
     const hipError_t e = a.D == 64 ? launch_shared_d<64>(prm, G, nset, a.n_pre, a.n_suf, a.stream)
                        : a.D == 128 ? launch_shared_d<128>(prm, G, nset, a.n_pre, a.n_suf, a.stream)
+                                    : hipErrorInvalidValue;
+    if (e != hipSuccess) {
+        *err = hipGetErrorString(e);
+        return (int)e;
+    }
+    return 0;
+}
+
+int launch_decode_multi(const MultiLaunch& a, const char** err) {
+    Params prm{};
+    prm.out = a.out;
+    prm.ws_o = a.ws_o;
+    prm.ws_ml = reinterpret_cast<float2*>(a.ws_ml);
+    prm.q = static_cast<const char*>(a.q);
+    prm.k = static_cast<const char*>(a.k);
+    prm.v = static_cast<const char*>(a.v);
+    prm.tables = a.tables;
+    prm.lens = a.lens;
+    prm.B = a.B;
+    prm.Hq = a.Hq;
+    prm.Hkv = a.Hkv;
+    prm.bs = a.bs;
+    int shift = 0;
+    while ((1 << shift) < a.bs) ++shift;
+    prm.bs_shift = shift;
+    prm.num_blocks = a.num_blocks;
+    prm.max_blocks = a.max_blocks;
+    prm.part_tokens = a.part_tokens;
+    prm.n_parts = a.n_parts;
+    prm.scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+    prm.q_starts = a.q_starts;
+    prm.total_q = a.total_q;
+    prm.max_q = a.max_q;
+    prm.n_tiles = a.n_tiles;
+    prm.pre_items = a.Hkv * a.n_tiles * a.n_parts * a.B;   // host-checked to fit
+    if (a.B == 0 || a.total_q == 0) return 0;
+    hipStream_t s = reinterpret_cast<hipStream_t>(a.stream);
+    const hipError_t e = a.D == 64 ? launch_multi_d<64>(prm, a.nset, s)
+                       : a.D == 128 ? launch_multi_d<128>(prm, a.nset, s)
                                     : hipErrorInvalidValue;
     if (e != hipSuccess) {
         *err = hipGetErrorString(e);

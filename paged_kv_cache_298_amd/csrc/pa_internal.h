@@ -67,9 +67,37 @@ struct SharedLaunch {
 constexpr int kPrefixTokens = PA_PREFIX_TOKENS;
 constexpr int kMaxSharedRows = 64;      // members x G query rows per KV head
 
+// Multi-query decode with a causal mask (pa_decode_multi), already validated on the host.
+struct MultiLaunch {
+    float* out;              // [total_q, Hq, D]
+    float* ws_o;             // [total_q, Hq, n_parts, D] (n_parts > 1 only)
+    float* ws_ml;            // [total_q, Hq, n_parts, 2]
+    const void* q;           // [total_q, Hq, D]
+    const void* k;
+    const void* v;
+    const int32_t* tables;
+    const int32_t* lens;
+    const int32_t* q_starts; // device [B + 1]
+    int32_t B, total_q, max_q, Hq, Hkv, D, bs, num_blocks, max_blocks;
+    int32_t nset;            // query tile = 16 nset rows
+    int32_t n_tiles, part_tokens, n_parts;
+    float scale;
+    void* stream;
+};
+
+// How pa_decode_multi splits its work: query tiles of 16 nset rows, token partitions of
+// part_tokens (a multiple of 16; one partition when that already gives enough waves).
+struct MultiPlan {
+    int32_t nset, n_tiles, part_tokens, n_parts;
+};
+MultiPlan multi_plan(int32_t B, int32_t max_q, int32_t Hq, int32_t Hkv, int32_t capacity);
+constexpr int kMultiMinWaves = 2048;    // split the tokens until this many items exist
+constexpr int kMultiMinPart = 256;      // ... but not below this many tokens per partition
+
 // Each returns 0 on success or a nonzero HIP error code (message in *err).
 int launch_decode(const DecodeLaunch& a, const char** err);
 int launch_decode_shared(const SharedLaunch& a, const char** err);
+int launch_decode_multi(const MultiLaunch& a, const char** err);
 int launch_reshape_and_cache(void* k_cache, void* v_cache, const void* key, const void* value,
                              const int32_t* slot_mapping, int32_t T, int32_t Hkv,
                              int32_t row_bytes, int32_t block_size, int32_t num_blocks,

@@ -35,6 +35,9 @@ _SIGS = {
     "pa_decode_shared": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_decode_shared_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_multi": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                               _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pa_decode_multi_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                     _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
@@ -162,6 +165,32 @@ def pa_decode_shared(out, q, k_cache, v_cache, block_tables, seq_lens, groups, m
                                  int(max_shared_tokens), B, Hq, Hkv, D, bs, nb, max_blocks,
                                  float(scale), _kv_dtype(k_cache), _ptr(workspace), ws_bytes,
                                  _stream(q, stream)))
+    return out
+
+
+def pa_decode_multi_workspace_bytes(B, total_q, max_q, Hq, Hkv, D, block_size, max_blocks):
+    return int(_lib.pa_decode_multi_workspace_bytes(B, total_q, max_q, Hq, Hkv, D, block_size,
+                                                    max_blocks))
+
+
+def pa_decode_multi(out, q, k_cache, v_cache, block_tables, seq_lens, q_starts, max_q, scale,
+                    workspace=None, stream=None):
+    """Causal multi-query attention: q [total_q, Hq, D] holds each sequence's last n_b
+    tokens (q_starts int32 [B + 1] on the device); query j of sequence b attends to tokens
+    0 .. seq_lens[b] - n_b + j. max_q: host bound on any n_b."""
+    total_q, Hq, D = q.shape
+    nb, Hkv, bs, _ = k_cache.shape
+    B = seq_lens.shape[0]
+    max_blocks = block_tables.shape[1]
+    need = pa_decode_multi_workspace_bytes(B, total_q, max_q, Hq, Hkv, D, bs, max_blocks)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.pa_decode_multi(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(block_tables), _ptr(seq_lens), _ptr(q_starts), B, total_q,
+                                int(max_q), Hq, Hkv, D, bs, nb, max_blocks, float(scale),
+                                _kv_dtype(k_cache), _ptr(workspace), ws_bytes,
+                                _stream(q, stream)))
     return out
 
 

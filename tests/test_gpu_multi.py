@@ -1,0 +1,140 @@
+"""Parity of pa_decode_multi (causal multi-query attention: prefill, prompt chunks, draft
+tokens) with the oracle, on an MI355X, through the C ABI.
+
+Each step writes the chunk's K/V with pa_reshape_and_cache, then runs pa_decode_multi.
+Max-abs error over every output element <= 2e-2 (bf16 caches, fp32 accumulation); at
+full size the oracle computes a seeded sample of rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_298_amd import workloads as W
+from tests._gpu_helpers import DEV, TOL, check_inputs, max_err, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_cache_298_amd import pa as _pa
+    return _pa
+
+
+def _check_chunks(wl):
+    qs = wl.q_starts
+    n = np.diff(qs)
+    assert qs[0] == 0 and qs[-1] == wl.q.shape[0] and np.all(n >= 0) and np.all(n <= wl.seq_lens)
+
+
+def _multi_gpu(pa, wl, repeat=1):
+    check_inputs(wl)
+    _check_chunks(wl)
+    k, v = to_dev(wl.k_cache), to_dev(wl.v_cache)
+    q, bt, sl, qs = to_dev(wl.q), to_dev(wl.block_tables), to_dev(wl.seq_lens), to_dev(wl.q_starts)
+    out = torch.full((wl.q.shape[0], wl.Hq, wl.D), float("nan"), dtype=torch.float32, device=DEV)
+    pa.pa_reshape_and_cache(k, v, to_dev(wl.new_key), to_dev(wl.new_value), to_dev(wl.slot_mapping))
+    max_q = int(np.diff(wl.q_starts).max(initial=0))
+    outs = []
+    for _ in range(repeat):
+        pa.pa_decode_multi(out, q, k, v, bt, sl, qs, max_q, wl.scale)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy().copy())
+    return outs, (k, v, bt, sl)
+
+
+def _multi_oracle(oracle, wl, rows=None):
+    kc, vc = oracle.reshape_and_cache(wl.k_cache, wl.v_cache, wl.new_key, wl.new_value,
+                                      wl.slot_mapping)
+    return oracle.decode_multi(wl.q, kc, vc, wl.block_tables, wl.seq_lens, wl.q_starts,
+                               wl.scale, rows=rows)
+
+
+def _parity(pa, oracle, wl, tag, rows=None):
+    n = np.diff(wl.q_starts)
+    note(f"multi {tag}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} bs={wl.block_size} "
+         f"lens[:6]={list(wl.seq_lens[:6])} n[:6]={list(n[:6])} total_q={int(wl.q_starts[-1])}")
+    (got,), _ = _multi_gpu(pa, wl)
+    ref = _multi_oracle(oracle, wl, rows=rows)
+    if rows is not None:
+        got = got.reshape(-1, wl.D)[rows]
+    assert np.all(np.isfinite(got))
+    err = max_err(got, ref)
+    note(f"  max abs err {err:.3e}")
+    assert err <= TOL[wl.dtype]
+    return got
+
+
+MULTI = [
+    # name, lens, n_new, Hq, Hkv, D, bs
+    ("tiny", [5, 16, 40], [5, 3, 17], 8, 2, 64, 16),
+    ("prompts", [300, 700], [300, 700], 32, 8, 128, 32),            # whole prompts (prefill)
+    ("chunks-g8", [1500, 2100], [256, 512], 64, 8, 128, 64),        # 66-group partitions
+    ("mixed", [40, 1, 333, 90, 17], [0, 1, 33, 90, 4], 16, 4, 64, 128),
+    ("g1", [100, 250, 64], [7, 250, 1], 4, 4, 128, 16),
+]
+
+
+@pytest.mark.parametrize("case", MULTI, ids=lambda c: c[0])
+def test_multi_matches_oracle(pa, oracle, case):
+    name, lens, n_new, Hq, Hkv, D, bs = case
+    wl = W.make_workload(f"mq-{name}", len(lens), Hq, Hkv, D, bs, lens, W.BF16,
+                         seed=sum(lens) + bs, n_new=n_new)
+    _parity(pa, oracle, wl, name)
+
+
+def test_draft_tokens_split_partitions(pa, oracle):
+    """Four draft tokens per sequence on ragged lengths: one query tile per (sequence, KV
+    head), so the tokens are split into partitions and merged."""
+    rng = np.random.default_rng(41)
+    lens = rng.integers(4, 1200, size=16)
+    wl = W.make_workload("mq-draft", 16, 32, 8, 128, 16, lens, W.BF16, seed=41, n_new=[4] * 16)
+    from paged_kv_cache_298_amd import pa as _pa
+    assert _pa.pa_decode_multi_workspace_bytes(16, 64, 4, 32, 8, 128, 16, wl.max_blocks) > 0
+    _parity(pa, oracle, wl, "draft")
+
+
+def test_one_query_per_sequence_matches_pa_decode(pa, oracle):
+    rng = np.random.default_rng(3)
+    lens = rng.integers(1, 900, size=12)
+    wl = W.make_workload("mq-one", 12, 32, 8, 128, 16, lens, W.BF16, seed=3, n_new=[1] * 12)
+    got = _parity(pa, oracle, wl, "one query")
+    dec = W.make_workload("mq-one", 12, 32, 8, 128, 16, lens, W.BF16, seed=3)
+    assert np.array_equal(dec.q, wl.q) and np.array_equal(dec.k_cache, wl.k_cache)
+    k, v = to_dev(dec.k_cache), to_dev(dec.v_cache)
+    pa.pa_reshape_and_cache(k, v, to_dev(dec.new_key), to_dev(dec.new_value), to_dev(dec.slot_mapping))
+    out = torch.empty((12, 32, 128), dtype=torch.float32, device=DEV)
+    pa.pa_decode(out, to_dev(dec.q), k, v, to_dev(dec.block_tables), to_dev(dec.seq_lens), dec.scale)
+    torch.cuda.synchronize()
+    assert max_err(got, out.cpu().numpy()) <= TOL[W.BF16]
+
+
+def test_multi_repeatable_bitwise(pa):
+    wl = W.make_workload("mq-rep", 3, 32, 8, 128, 16, [400, 90, 1300], W.BF16, seed=5,
+                         n_new=[64, 90, 8])
+    outs, _ = _multi_gpu(pa, wl, repeat=2)
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_placement_leaves_multi_bitwise_equal(pa):
+    outs = []
+    for placement in ("permute", "identity"):
+        wl = W.make_workload("mq-pl", 3, 32, 8, 128, 16, [400, 90, 1300], W.BF16, seed=5,
+                             n_new=[64, 90, 8], placement=placement)
+        (o,), _ = _multi_gpu(pa, wl)
+        outs.append(o)
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_draft_tokens_llama3_batch_sampled(pa, oracle):
+    """The Llama-3-8B batch's lengths with four draft tokens per sequence, at full size;
+    the oracle computes 256 seeded rows."""
+    rng = np.random.default_rng(29802)
+    lens = rng.integers(1, 4097, size=64).astype(np.int32)
+    lens = np.maximum(lens, 4)
+    wl = W.make_workload("mq-llama3-draft", 64, 32, 8, 128, 16, lens, W.BF16, seed=29802,
+                         max_blocks=256, n_new=[4] * 64)
+    rows = np.sort(np.random.default_rng(7).choice(int(wl.q_starts[-1]) * 32, 256, replace=False)).astype(np.int32)
+    _parity(pa, oracle, wl, "llama3 draft", rows=rows)
