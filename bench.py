@@ -219,6 +219,73 @@ def _shared_prefix(torch, pa, W, dev, args):
         "speedup_vs_pa_decode": round(pl["mean"] / sh["mean"], 3)}), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def _multi_query(torch, pa, W, dev, args):
+    """pa_decode_multi on two batches; one JSON line each.
+
+    draft: the Llama-3-8B batch's 64 lengths (at least 4) with the last 4 tokens of each
+    sequence as queries (speculative decoding's check of 4 draft tokens). HBM-bound: the
+    KV bytes are those of a decode step.
+    chunks: 4 sequences whose newest 1024 tokens are a prompt chunk, after 0, 1024, 2048
+    and 3072 cached tokens (chunked prefill). Matrix-core bound: 4 D flops per (query
+    head, visible token), bf16 MFMA peak 2.5 PFLOP/s.
+    Each is the cache write of the chunk followed by pa_decode_multi, timed with HIP events
+    around each pa_decode_multi call, rotating enough replicas to exceed 1 GiB.
+    """
+    rng = np.random.default_rng(29802)
+    L2 = np.maximum(rng.integers(1, 4097, size=64).astype(np.int32), 4)
+    cases = [
+        ("draft-4-llama3-8b", W.make_workload("draft", 64, 32, 8, 128, 16, L2, W.BF16, 29802,
+                                             max_blocks=256, poison=False, n_new=[4] * 64)),
+        ("chunk-1024x4-llama3-8b", W.make_workload("chunks", 4, 32, 8, 128, 16,
+                                                   [1024, 2048, 3072, 4096], W.BF16, 29806,
+                                                   max_blocks=256, poison=False,
+                                                   n_new=[1024] * 4)),
+    ]
+    steps = max(20, min(args.steps, 200))
+    for name, wl in cases:
+        qs = wl.q_starts
+        n = np.diff(qs)
+        max_q, total_q = int(n.max()), int(qs[-1])
+        kv = wl.kv_bytes()
+        vis = sum(int(L - k + j + 1) for L, k in zip(wl.seq_lens, n) for j in range(int(k)))
+        flops = 4.0 * wl.D * wl.Hq * vis
+        ws_bytes = pa.pa_decode_multi_workspace_bytes(wl.B, total_q, max_q, wl.Hq, wl.Hkv, wl.D,
+                                                      wl.block_size, wl.max_blocks)
+        per_replica = 2 * wl.k_cache.nbytes + wl.q.nbytes
+        R = args.replicas or max(2, math.ceil((1 << 30) / per_replica))
+        reps = [dict(q=_to_dev(wl.q, torch, dev), k=_to_dev(wl.k_cache, torch, dev),
+                     v=_to_dev(wl.v_cache, torch, dev), bt=_to_dev(wl.block_tables, torch, dev),
+                     sl=_to_dev(wl.seq_lens, torch, dev), qs=_to_dev(qs, torch, dev),
+                     nk=_to_dev(wl.new_key, torch, dev), nv=_to_dev(wl.new_value, torch, dev),
+                     slots=_to_dev(wl.slot_mapping, torch, dev),
+                     out=torch.empty((total_q, wl.Hq, wl.D), dtype=torch.float32, device=dev),
+                     ws=torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev))
+                for _ in range(R)]
+        stream = torch.cuda.current_stream(dev)
+        for r in reps:
+            pa.pa_reshape_and_cache(r["k"], r["v"], r["nk"], r["nv"], r["slots"], stream=stream)
+
+        def multi(r):
+            pa.pa_decode_multi(r["out"], r["q"], r["k"], r["v"], r["bt"], r["sl"], r["qs"], max_q,
+                               wl.scale, workspace=r["ws"], stream=stream)
+
+        t = _per_call_us(torch, multi, reps, steps, args.warmup, stream)
+        sec = t["mean"] * 1e-6
+        line = {"bench": "multi_query", "workload": name, "B": wl.B, "queries": total_q,
+                "max_q": max_q, "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "block_size": wl.block_size,
+                "seq_lens": [int(x) for x in wl.seq_lens] if wl.B <= 8 else "llama3-8b batch",
+                "replicas_rotated": R, "decode_multi_us": t, "kv_bytes": kv,
+                "kv_GBps": round(kv / sec / 1e9, 1), "kv_frac_of_hbm": round(kv / sec / 1e9 / HBM_PEAK_GBS, 4),
+                "flops": flops, "TFLOPs": round(flops / sec / 1e12, 1),
+                "mfma_frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        print(json.dumps(line), flush=True)
+        del reps
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +304,9 @@ def main():
     ap.add_argument("--shared-prefix", action="store_true",
                     help="the shared-prefix batch through pa_decode_shared and pa_decode; "
                          "one JSON line")
+    ap.add_argument("--multi-query", action="store_true",
+                    help="pa_decode_multi on draft tokens (Llama-3-8B batch) and on prompt "
+                         "chunks; one JSON line each")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -258,6 +328,9 @@ def main():
         return
     if args.shared_prefix:
         _shared_prefix(torch, pa, W, dev, args)
+        return
+    if args.multi_query:
+        _multi_query(torch, pa, W, dev, args)
         return
     _log(f"generating workload {args.config}")
     wl = W.config(args.config, poison=False)

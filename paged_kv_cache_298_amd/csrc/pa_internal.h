@@ -91,8 +91,14 @@ struct MultiPlan {
     int32_t nset, n_tiles, part_tokens, n_parts;
 };
 MultiPlan multi_plan(int32_t B, int32_t max_q, int32_t Hq, int32_t Hkv, int32_t capacity);
-constexpr int kMultiMinWaves = 2048;    // split the tokens until this many items exist
-constexpr int kMultiMinPart = 256;      // ... but not below this many tokens per partition
+#ifndef PA_MULTI_MIN_WAVES
+#define PA_MULTI_MIN_WAVES 2048
+#endif
+#ifndef PA_MULTI_MIN_PART
+#define PA_MULTI_MIN_PART 256
+#endif
+constexpr int kMultiMinWaves = PA_MULTI_MIN_WAVES;   // split the tokens until this many items exist
+constexpr int kMultiMinPart = PA_MULTI_MIN_PART;     // ... but not below this many tokens per partition
 
 // Each returns 0 on success or a nonzero HIP error code (message in *err).
 int launch_decode(const DecodeLaunch& a, const char** err);

@@ -207,3 +207,42 @@ def test_decode_shared_workspace_and_empty_batch():
     rows = 128 * 32 * n
     assert pa.pa_decode_shared_workspace_bytes(128, 32, 128, 16, 144, 2032) == _up(rows * 128 * 4) + rows * 8
     assert pa.pa_decode_shared_workspace_bytes(0, 32, 128, 16, 144, 2032) == 0
+
+
+def _multi(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, qs=FAKE, B=8, tq=32, mq=4,
+             Hq=32, Hkv=8, D=128, bs=16, nb=64, mb=8, scale=0.1, dt=pa.PA_BF16, ws=None, wsb=0,
+             stream=None)
+    a.update(kw)
+    return pa._lib.pa_decode_multi(a["out"], a["q"], a["k"], a["v"], a["bt"], a["sl"], a["qs"],
+                                   a["B"], a["tq"], a["mq"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                                   a["nb"], a["mb"], a["scale"], a["dt"], a["ws"], a["wsb"],
+                                   a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=pa.PA_F32), pa.PA_ERR_UNSUPPORTED),          # bf16 only
+    (dict(bs=8), pa.PA_ERR_UNSUPPORTED),
+    (dict(D=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(Hq=30), pa.PA_ERR_INVALID_ARG),
+    (dict(qs=None), pa.PA_ERR_INVALID_ARG),
+    (dict(mq=0), pa.PA_ERR_INVALID_ARG),                  # queries but no bound
+    (dict(tq=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(mb=256), pa.PA_ERR_INVALID_ARG),                # 4096-token capacity: split, no workspace
+    (dict(mb=256, ws=FAKE, wsb=16), pa.PA_ERR_INVALID_ARG),
+])
+def test_decode_multi_rejects_bad_arguments(kw, status):
+    assert _multi(**kw) == status
+    assert pa._lib.pa_last_error().decode().startswith("pa_decode_multi")
+
+
+def test_decode_multi_workspace_and_empty_batch():
+    assert _multi(B=0, out=None, q=None) == pa.PA_OK
+    assert _multi(tq=0, out=None, q=None) == pa.PA_OK
+    # four draft tokens on 64 sequences of up to 4096 tokens: 64 x 8 units, split into 4
+    # partitions of 1024 tokens; records [256 queries x 32 heads x 4, D] plus (m, l)
+    rows = 256 * 32 * 4
+    assert pa.pa_decode_multi_workspace_bytes(64, 256, 4, 32, 8, 128, 16, 256) == _up(rows * 128 * 4) + rows * 8
+    # 1024-token chunks of 4 sequences: 64 tiles each, enough items without a split
+    assert pa.pa_decode_multi_workspace_bytes(4, 4096, 1024, 32, 8, 128, 16, 256) == 0
+    assert pa.pa_decode_multi_workspace_bytes(0, 4, 4, 32, 8, 128, 16, 256) == 0
