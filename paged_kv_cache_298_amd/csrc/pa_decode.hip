@@ -1299,100 +1299,124 @@ __device__ __forceinline__ void multi_item(const Params& p, int id) {
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    for (int t0g = 0; t0g < ng; t0g += U) {
+    // scores of one group for every set: y[s][o + i] for tokens r + 4i of the group
+    auto qk = [&](const Item& kit, float (&y)[NSET][8], int o) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int t = t0g + u;
-            Item& kit = ring[2 * u];
-            Item& vit = ring[2 * u + 1];
-            const bool live = t < ng;
-            const int valid = min(16, ntok - 16 * t);
-            const int tg = t0 + 16 * t;          // first token of the group
-            float y[NSET][4];
-            uint32_t pw[NSET][2];
-            if (live) {
+        for (int s = 0; s < NSET; ++s) {
+            f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < NSET; ++s) {
-                    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+            for (int k = 0; k < NQ; ++k)
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, kit.q[k]),
+                    __builtin_bit_cast(bf16x8_t, qf[s][k]), sc, 0, 0, 0);
 #pragma unroll
-                    for (int k = 0; k < NQ; ++k)
-                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, kit.q[k]),
-                            __builtin_bit_cast(bf16x8_t, qf[s][k]), sc, 0, 0, 0);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) y[s][i] = sc[i] * cl2;
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            issue_k(t + U, kit);
-            __builtin_amdgcn_sched_barrier(0);
-            if (live) {
-                // the causal edge (and the partition's end) fall inside this group
-                const bool edge = tg + 15 > pos_first;
-#pragma unroll
-                for (int s = 0; s < NSET; ++s) {
-                    if (edge) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) y[s][i] = (tg + r + 4 * i <= pos_c[s]) ? y[s][i] : -INFINITY;
-                    }
-                    const float mx = fmaxf(fmaxf(y[s][0], y[s][1]), fmaxf(y[s][2], y[s][3]));
-                    const float m_new = fmaxf(m_run[s], rows_max(mx));
-                    // a column that has seen no token yet keeps m = -inf: use 0 as its
-                    // reference so that its factors are exactly 0 instead of NaN
-                    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-                    const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_ref);   // per column
-                    m_run[s] = m_new;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float ai = __shfl(alpha, 4 * r + i);
-#pragma unroll
-                        for (int e = 0; e < EV; ++e) acc[s][e][i] *= ai;
-                    }
-                    const bf16x2_t p01 = __builtin_convertvector(
-                        (f32x2_t){__builtin_amdgcn_exp2f(y[s][0] - m_ref), __builtin_amdgcn_exp2f(y[s][1] - m_ref)}, bf16x2_t);
-                    const bf16x2_t p23 = __builtin_convertvector(
-                        (f32x2_t){__builtin_amdgcn_exp2f(y[s][2] - m_ref), __builtin_amdgcn_exp2f(y[s][3] - m_ref)}, bf16x2_t);
-                    pw[s][0] = __builtin_bit_cast(uint32_t, p01);
-                    pw[s][1] = __builtin_bit_cast(uint32_t, p23);
-                    l_run[s] = l_run[s] * alpha + ((lo_bf16(pw[s][0]) + hi_bf16(pw[s][0])) +
-                                                   (lo_bf16(pw[s][1]) + hi_bf16(pw[s][1])));
-                }
-                if (valid < 16) {
-                    // rows past the partition's last token may hold anything (the tail of
-                    // the sequence's last block): their probabilities are 0, their values too
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        if (r + 4 * k >= valid) {
-                            if constexpr (WV == 16) {
-                                vit.q[k] = u32x4_t{0u, 0u, 0u, 0u};
-                            } else {
-                                vit.q[k >> 1][(k & 1) * 2] = 0u;
-                                vit.q[k >> 1][(k & 1) * 2 + 1] = 0u;
-                            }
-                        }
-                    }
-                }
-#pragma unroll
-                for (int w = 0; w < WV / 4; ++w) {
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const uint32_t sel = h ? 0x07060302u : 0x05040100u;
-                        const u32x2_t bv = {__builtin_amdgcn_perm(vword(vit, 1, w), vword(vit, 0, w), sel),
-                                            __builtin_amdgcn_perm(vword(vit, 3, w), vword(vit, 2, w), sel)};
-#pragma unroll
-                        for (int s = 0; s < NSET; ++s) {
-                            const u32x2_t av = {pw[s][0], pw[s][1]};
-                            acc[s][2 * w + h] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                                __builtin_bit_cast(s16x4_t, av), __builtin_bit_cast(s16x4_t, bv),
-                                acc[s][2 * w + h], 0, 0, 0);
-                        }
-                    }
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            issue_v(t + U, vit);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < 4; ++i) y[s][o + i] = sc[i] * cl2;
         }
+    };
+    // rows past `valid` of a V item may hold anything: their probabilities are 0, their
+    // values are zeroed too
+    auto zero_rows = [&](Item& vit, int valid) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (r + 4 * k >= valid) {
+                if constexpr (WV == 16) {
+                    vit.q[k] = u32x4_t{0u, 0u, 0u, 0u};
+                } else {
+                    vit.q[k >> 1][(k & 1) * 2] = 0u;
+                    vit.q[k >> 1][(k & 1) * 2 + 1] = 0u;
+                }
+            }
+        }
+    };
+
+    // Two groups (32 tokens) per step: both score tiles, one online-softmax update, and PV
+    // on v_mfma_f32_16x16x32_bf16 whose k index runs over the 8 tokens a lane holds (r + 4i
+    // of the first group, then of the second), for the probabilities and V alike.
+    for (int t = 0; t < ng; t += 2) {
+        Item& k0 = ring[0];
+        Item& v0 = ring[1];
+        Item& k1 = ring[2];
+        Item& v1 = ring[3];
+        const bool live1 = t + 1 < ng;
+        const int tg = t0 + 16 * t;              // first token of the pair
+        float y[NSET][8];
+        qk(k0, y, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_k(t + 2, k0);
+        __builtin_amdgcn_sched_barrier(0);
+        qk(k1, y, 4);                            // a re-read of the last group when !live1
+        __builtin_amdgcn_sched_barrier(0);
+        issue_k(t + 3, k1);
+        __builtin_amdgcn_sched_barrier(0);
+        // the causal edge, the partition's end or a missing second group fall in this pair
+        const bool edge = tg + 31 > pos_first || !live1;
+        uint32_t pw[NSET][4];
+#pragma unroll
+        for (int s = 0; s < NSET; ++s) {
+            if (edge) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int tok = tg + (i >> 2) * 16 + r + 4 * (i & 3);
+                    const bool ok = tok <= pos_c[s] && (i < 4 || live1);
+                    y[s][i] = ok ? y[s][i] : -INFINITY;
+                }
+            }
+            float mx = y[s][0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, y[s][i]);
+            const float m_new = fmaxf(m_run[s], rows_max(mx));
+            // a column that has seen no token yet keeps m = -inf: use 0 as its reference so
+            // that its factors are exactly 0 instead of NaN
+            const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_ref);   // per column
+            m_run[s] = m_new;
+            // rescale only when some column's maximum moved (a factor of 1 is exact)
+            if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __shfl(alpha, 4 * r + i);
+#pragma unroll
+                    for (int e = 0; e < EV; ++e) acc[s][e][i] *= ai;
+                }
+            }
+            float ls = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const bf16x2_t pp = __builtin_convertvector(
+                    (f32x2_t){__builtin_amdgcn_exp2f(y[s][2 * w] - m_ref),
+                              __builtin_amdgcn_exp2f(y[s][2 * w + 1] - m_ref)}, bf16x2_t);
+                pw[s][w] = __builtin_bit_cast(uint32_t, pp);
+                ls += lo_bf16(pw[s][w]) + hi_bf16(pw[s][w]);
+            }
+            l_run[s] = l_run[s] * alpha + ls;
+        }
+        if (edge) {
+            zero_rows(v0, ntok - 16 * t);
+            zero_rows(v1, live1 ? ntok - 16 * (t + 1) : 0);
+        }
+#pragma unroll
+        for (int w = 0; w < WV / 4; ++w) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+                const u32x4_t bv = {__builtin_amdgcn_perm(vword(v0, 1, w), vword(v0, 0, w), sel),
+                                    __builtin_amdgcn_perm(vword(v0, 3, w), vword(v0, 2, w), sel),
+                                    __builtin_amdgcn_perm(vword(v1, 1, w), vword(v1, 0, w), sel),
+                                    __builtin_amdgcn_perm(vword(v1, 3, w), vword(v1, 2, w), sel)};
+#pragma unroll
+                for (int s = 0; s < NSET; ++s) {
+                    const u32x4_t av = {pw[s][0], pw[s][1], pw[s][2], pw[s][3]};
+                    acc[s][2 * w + h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv),
+                        acc[s][2 * w + h], 0, 0, 0);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue_v(t + 2, v0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_v(t + 3, v1);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // output row qr = 16 s + 4 r + i sits in lane (r, c), columns c*EV..; its (max, sum)
