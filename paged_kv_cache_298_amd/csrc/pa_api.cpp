@@ -109,7 +109,7 @@ namespace pa_internal {
 MultiPlan multi_plan(int32_t B, int32_t max_q, int32_t Hq, int32_t Hkv, int32_t capacity) {
     MultiPlan m;
     const int64_t rows = (int64_t)max_q * (Hq / Hkv);
-    m.nset = rows > 32 ? 4 : (rows > 16 ? 2 : 1);
+    m.nset = rows > 32 && PA_MULTI_MAX_NSET >= 4 ? 4 : (rows > 16 ? 2 : 1);
     m.n_tiles = (int32_t)std::max<int64_t>(1, (rows + 16 * m.nset - 1) / (16 * m.nset));
     int64_t P = std::max<int64_t>(16, ((int64_t)capacity + 15) / 16 * 16);
     const int64_t units = (int64_t)B * Hkv * m.n_tiles;

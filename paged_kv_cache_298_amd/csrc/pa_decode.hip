@@ -1173,9 +1173,13 @@ __device__ __forceinline__ void multi_item(const Params& p, int id) {
     static_assert(D == 64 || D == 128, "head size");
 
     const int lane = threadIdx.x & 63;
+    // item order: KV head fastest (the heads spread over the XCDs), then query tile from
+    // the last (a chunk's later tiles see the most tokens, so they start first), then
+    // partition, then sequence: the tiles of one (sequence, KV head) run together on one
+    // XCD and share its L2
     const int g = id % p.Hkv;
     int rest = id / p.Hkv;
-    const int tile = rest % p.n_tiles;
+    const int tile = p.n_tiles - 1 - rest % p.n_tiles;
     rest /= p.n_tiles;
     const int part = rest % p.n_parts;
     const int b = rest / p.n_parts;

@@ -94,6 +94,9 @@ MultiPlan multi_plan(int32_t B, int32_t max_q, int32_t Hq, int32_t Hkv, int32_t 
 #ifndef PA_MULTI_MIN_WAVES
 #define PA_MULTI_MIN_WAVES 2048
 #endif
+#ifndef PA_MULTI_MAX_NSET
+#define PA_MULTI_MAX_NSET 4
+#endif
 #ifndef PA_MULTI_MIN_PART
 #define PA_MULTI_MIN_PART 256
 #endif

@@ -36,7 +36,7 @@ def run(lens, n_new, Hq, Hkv, bs, max_blocks):
     for item in range(Hkv * n_tiles * n_parts * B):
         g = item % Hkv
         rest = item // Hkv
-        tile = rest % n_tiles
+        tile = n_tiles - 1 - rest % n_tiles
         rest //= n_tiles
         part = rest % n_parts
         b = rest // n_parts
