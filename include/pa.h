@@ -288,6 +288,47 @@ int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block);
 int32_t pa_alloc_num_free(const pa_allocator* a);
 /* copies the free stack, bottom to top, into out (capacity cap); returns its length */
 int32_t pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap);
+/* tokens per block the allocator was created with */
+int32_t pa_alloc_block_size(const pa_allocator* a);
+
+/* ------------------------------------------------------------------ prefix cache */
+
+/*
+ * A prefix cache over an allocator ([P2] section 5, "The relationship to prefix
+ * caching": hash the token ids of each block, keep a hash -> block map, and let a new
+ * sequence whose leading blocks are cached point at them). A block is found by its own
+ * tokens and all the tokens before it (the chain from the sequence's first block), and
+ * only full blocks are cached. Host memory only, not thread-safe; the allocator must
+ * outlive the cache, and the cache holds one reference of its own on every cached block.
+ */
+typedef struct pa_prefix_cache pa_prefix_cache;
+
+pa_prefix_cache* pa_pcache_create(pa_allocator* a);
+/* drops the cache's references (a cached block nobody else holds returns to the free list) */
+void pa_pcache_destroy(pa_prefix_cache* c);
+/*
+ * Table for a new sequence of n_tokens prompt tokens: the longest run of leading full
+ * blocks found in the cache is shared (one more reference each), the remaining
+ * ceil(n_tokens / block_size) - hits blocks are allocated. When fewer blocks are free
+ * than needed, cached blocks no sequence holds are released, least recently used first.
+ * *n_table = blocks in table (<= table_cap), *n_cached = tokens whose K/V the shared
+ * blocks already hold (hits * block_size). PA_ERR_NO_BLOCKS leaves everything unchanged.
+ */
+int32_t pa_pcache_acquire(pa_prefix_cache* c, const int32_t* tokens, int32_t n_tokens,
+                          int32_t* table, int32_t table_cap, int32_t* n_table,
+                          int32_t* n_cached);
+/*
+ * Make the full blocks of a sequence whose K/V the caller has written findable: block i
+ * of table (i < n_tokens / block_size) is cached under tokens[0 .. (i+1) block_size) and
+ * gains the cache's reference, unless an equal block is already cached (then that entry
+ * is only marked used).
+ */
+int32_t pa_pcache_publish(pa_prefix_cache* c, const int32_t* tokens, int32_t n_tokens,
+                          const int32_t* table, int32_t n_table);
+/* release up to n cached blocks no sequence holds, least recently used first; returns
+ * how many were released */
+int32_t pa_pcache_evict(pa_prefix_cache* c, int32_t n);
+int32_t pa_pcache_num_entries(const pa_prefix_cache* c);
 
 #ifdef __cplusplus
 }

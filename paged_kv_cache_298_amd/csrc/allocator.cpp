@@ -166,6 +166,8 @@ int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block) {
     return a->refcount[(size_t)block];
 }
 
+int32_t pa_alloc_block_size(const pa_allocator* a) { return a ? a->block_size : 0; }
+
 int32_t pa_alloc_num_free(const pa_allocator* a) {
     if (!a) return bad("pa_alloc_num_free: null allocator");
     return (int32_t)a->free_stack.size();

@@ -53,6 +53,13 @@ _SIGS = {
     "pa_alloc_refcount": (_i32, [_vp, _i32]),
     "pa_alloc_num_free": (_i32, [_vp]),
     "pa_alloc_free_list": (_i32, [_vp, _vp, _i32]),
+    "pa_alloc_block_size": (_i32, [_vp]),
+    "pa_pcache_create": (_vp, [_vp]),
+    "pa_pcache_destroy": (None, [_vp]),
+    "pa_pcache_acquire": (_i32, [_vp, _vp, _i32, _vp, _i32, _P32, _P32]),
+    "pa_pcache_publish": (_i32, [_vp, _vp, _i32, _vp, _i32]),
+    "pa_pcache_evict": (_i32, [_vp, _i32]),
+    "pa_pcache_num_entries": (_i32, [_vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -233,7 +240,7 @@ class BlockAllocator:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h:
+        if h and _lib is not None:          # not during interpreter shutdown
             _lib.pa_alloc_destroy(h)
             self._h = None
 
@@ -283,3 +290,47 @@ class BlockAllocator:
         out = self._np.zeros(max(self.num_blocks, 1), dtype=self._np.int32)
         n = _lib.pa_alloc_free_list(self._h, out.ctypes.data_as(_vp), self.num_blocks)
         return [int(x) for x in out[:n]]
+
+
+class PrefixCache:
+    """The prefix cache over a BlockAllocator (pa_pcache_*): full blocks found by their
+    token ids and everything before them are shared by new sequences. Host only."""
+
+    def __init__(self, allocator):
+        self._alloc = allocator          # keeps the allocator alive as long as the cache
+        self._np = allocator._np
+        h = _lib.pa_pcache_create(allocator._h)
+        if not h:
+            raise PaError(PA_ERR_INVALID_ARG, _lib.pa_last_error().decode())
+        self._h = ctypes.c_void_p(h)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:          # not during interpreter shutdown
+            _lib.pa_pcache_destroy(h)
+            self._h = None
+
+    def acquire(self, tokens):
+        """Table for a new sequence with these prompt tokens: (table, cached_tokens)."""
+        t = self._np.ascontiguousarray(tokens, dtype=self._np.int32)
+        bs = self._alloc.block_size
+        cap = max((t.shape[0] + bs - 1) // bs, 1)
+        out = self._np.zeros(cap, dtype=self._np.int32)
+        n, cached = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.pa_pcache_acquire(self._h, t.ctypes.data_as(_vp), t.shape[0],
+                                      out.ctypes.data_as(_vp), cap, ctypes.byref(n),
+                                      ctypes.byref(cached)))
+        return [int(x) for x in out[:n.value]], cached.value
+
+    def publish(self, tokens, table):
+        t = self._np.ascontiguousarray(tokens, dtype=self._np.int32)
+        tb = self._np.ascontiguousarray(table, dtype=self._np.int32)
+        _check(_lib.pa_pcache_publish(self._h, t.ctypes.data_as(_vp), t.shape[0],
+                                      tb.ctypes.data_as(_vp), tb.shape[0]))
+
+    def evict(self, n):
+        r = _lib.pa_pcache_evict(self._h, int(n))
+        return _check(r) if r < 0 else int(r)
+
+    def num_entries(self):
+        return int(_lib.pa_pcache_num_entries(self._h))
