@@ -1284,11 +1284,15 @@ __device__ __forceinline__ void multi_item(const Params& p, int id) {
     };
 
     f32x4_t acc[NSET][EV];
-    float m_run[NSET], l_run[NSET];
+    // the softmax sums of output rows 4r + i, accumulated on the matrix cores as P times
+    // a column of ones (the same rounded probabilities the PV product uses)
+    f32x4_t lsum[NSET];
+    float m_run[NSET];
+    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0
 #pragma unroll
     for (int s = 0; s < NSET; ++s) {
         m_run[s] = -INFINITY;
-        l_run[s] = 0.f;
+        lsum[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < EV; ++e) acc[s][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -1381,18 +1385,19 @@ __device__ __forceinline__ void multi_item(const Params& p, int id) {
                     const float ai = __shfl(alpha, 4 * r + i);
 #pragma unroll
                     for (int e = 0; e < EV; ++e) acc[s][e][i] *= ai;
+                    lsum[s][i] *= ai;
                 }
             }
-            float ls = 0.f;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const bf16x2_t pp = __builtin_convertvector(
                     (f32x2_t){__builtin_amdgcn_exp2f(y[s][2 * w] - m_ref),
                               __builtin_amdgcn_exp2f(y[s][2 * w + 1] - m_ref)}, bf16x2_t);
                 pw[s][w] = __builtin_bit_cast(uint32_t, pp);
-                ls += lo_bf16(pw[s][w]) + hi_bf16(pw[s][w]);
             }
-            l_run[s] = l_run[s] * alpha + ls;
+            const u32x4_t av = {pw[s][0], pw[s][1], pw[s][2], pw[s][3]};
+            lsum[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, ones), lsum[s], 0, 0, 0);
         }
         if (edge) {
             zero_rows(v0, ntok - 16 * t);
@@ -1423,15 +1428,14 @@ __device__ __forceinline__ void multi_item(const Params& p, int id) {
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // output row qr = 16 s + 4 r + i sits in lane (r, c), columns c*EV..; its (max, sum)
-    // were kept per column qr
+    // output row qr = 16 s + 4 r + i sits in lane (r, c), columns c*EV..; its maximum was
+    // kept per column qr, its sum in lsum[s][i]
 #pragma unroll
     for (int s = 0; s < NSET; ++s) {
-        const float lcol = rows_sum(l_run[s]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int qr = 16 * s + 4 * r + i;
-            const float lr = __shfl(lcol, 4 * r + i);
+            const float lr = lsum[s][i];
             const float mr = __shfl(m_run[s], 4 * r + i);
             if (qr < M) {
                 const int row = row0 + qr;
