@@ -446,6 +446,10 @@ int32_t pa_decode_multi(float* out, const void* q, const void* k_cache, const vo
         return fail(PA_ERR_INVALID_ARG, "pa_decode_multi: max_blocks * block_size exceeds 2^30");
     if (total_q > 0 && max_q == 0)
         return fail(PA_ERR_INVALID_ARG, "pa_decode_multi: max_q is 0 with %d queries", total_q);
+    // query rows per sequence (max_q x G) and rows in all (total_q x Hq) are int on the device
+    if ((int64_t)max_q * (Hq / Hkv) > ((int64_t)1 << 30) || (int64_t)total_q * Hq > 0x7fffffff)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_multi: %d queries x %d heads exceed the row range",
+                    total_q, Hq);
     if (D != 64 && D != 128)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode_multi: head_dim %d not built (64, 128)", D);
     if (block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128)

@@ -15,6 +15,20 @@ FAKE = ctypes.c_void_p(0x100000)     # aligned, never dereferenced: every call b
                                      # validation before it could reach the device
 
 
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+# A validation mistake in one of these cases would launch a kernel on the fake addresses:
+# on a machine with a GPU they do not run at all.
+pytestmark = pytest.mark.skipif(_gpu_visible(), reason="host-validation tests pass fake device "
+                                "addresses; they run only where no GPU is visible")
+
+
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -228,6 +242,8 @@ def _multi(**kw):
     (dict(qs=None), pa.PA_ERR_INVALID_ARG),
     (dict(mq=0), pa.PA_ERR_INVALID_ARG),                  # queries but no bound
     (dict(tq=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(mq=(1 << 28) + 1), pa.PA_ERR_UNSUPPORTED),      # over 2^30 query rows per sequence
+    (dict(tq=1 << 27), pa.PA_ERR_UNSUPPORTED),            # 2^27 x 32 rows in all
     (dict(mb=256), pa.PA_ERR_INVALID_ARG),                # 4096-token capacity: split, no workspace
     (dict(mb=256, ws=FAKE, wsb=16), pa.PA_ERR_INVALID_ARG),
 ])
