@@ -30,7 +30,9 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode attention effective KV GB/s (% of HBM peak); µs per decode step"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pa_decode.json")
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_298_amd", "csrc", "pa_decode.hip")
+# the sources the decode kernels are compiled from (the traffic summary is tied to them)
+DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_298_amd", "csrc", f)
+               for f in ("pa_decode.hip", "pa_device.h")]
 
 
 def _log(msg):
@@ -45,8 +47,11 @@ def _to_dev(a, torch, dev):
 
 
 def _decode_source_sha():
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in DECODE_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic_for(config_name):
