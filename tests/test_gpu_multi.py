@@ -74,6 +74,8 @@ MULTI = [
     ("chunks-g8", [1500, 2100], [256, 512], 64, 8, 128, 64),        # 66-group partitions
     ("mixed", [40, 1, 333, 90, 17], [0, 1, 33, 90, 4], 16, 4, 64, 128),
     ("g1", [100, 250, 64], [7, 250, 1], 4, 4, 128, 16),
+    ("d64-g8-bs64", [700, 130, 1], [70, 130, 1], 64, 8, 64, 64),   # one-token prompt
+    ("g2-long", [3000, 2500], [40, 1], 16, 8, 128, 32),             # split partitions, G=2
 ]
 
 
@@ -138,3 +140,20 @@ def test_draft_tokens_llama3_batch_sampled(pa, oracle):
                          max_blocks=256, n_new=[4] * 64)
     rows = np.sort(np.random.default_rng(7).choice(int(wl.q_starts[-1]) * 32, 256, replace=False)).astype(np.int32)
     _parity(pa, oracle, wl, "llama3 draft", rows=rows)
+
+
+def test_loose_max_q_bound_and_empty_chunks(pa, oracle):
+    """max_q larger than any chunk (it only sizes the tiles), and a batch in which most
+    sequences have no queries at all."""
+    wl = W.make_workload("mq-loose", 5, 32, 8, 128, 16, [50, 900, 17, 333, 64], W.BF16, seed=77,
+                         n_new=[0, 9, 0, 0, 2])
+    _check_chunks(wl)
+    k, v = to_dev(wl.k_cache), to_dev(wl.v_cache)
+    pa.pa_reshape_and_cache(k, v, to_dev(wl.new_key), to_dev(wl.new_value), to_dev(wl.slot_mapping))
+    out = torch.full((11, 32, 128), float("nan"), dtype=torch.float32, device=DEV)
+    note("multi loose max_q=64 for chunks of at most 9")
+    pa.pa_decode_multi(out, to_dev(wl.q), k, v, to_dev(wl.block_tables), to_dev(wl.seq_lens),
+                       to_dev(wl.q_starts), 64, wl.scale)
+    torch.cuda.synchronize()
+    ref = _multi_oracle(oracle, wl)
+    assert max_err(out.cpu().numpy(), ref) <= TOL[W.BF16]
