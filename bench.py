@@ -89,6 +89,20 @@ def _cpu_baseline(wl, budget_s):
                       f"repeated {reps}x, {el:.1f} s"}
 
 
+def _cpu_timed(run, budget_s):
+    """Repeat the oracle call `run` for about budget_s seconds (at least once); returns
+    (seconds per call, repetitions, elapsed, threads)."""
+    from oracle import oracle as orc
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        run()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 200:
+            break
+    return el / reps, reps, el, orc.max_threads()
+
+
 def _copy_calibration(torch, pa, dev, launches=5):
     """pa_copy_blocks of 2048 distinct blocks onto 2048 others, K and V, bf16, Hkv=8,
     bs=16, D=128 (32 KiB per block and cache): 128 MiB read and 128 MiB written per launch."""
@@ -213,6 +227,18 @@ def _shared_prefix(torch, pa, W, dev, args):
     st = _per_call_us(torch, step, reps, steps, args.warmup, stream)
     sh = _per_call_us(torch, shared, reps, steps, args.warmup, stream)
     pl = _per_call_us(torch, plain, reps, steps, args.warmup, stream)
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as orc
+        kc, vc = orc.copy_blocks(wl.k_cache, wl.v_cache, wl.cow_pairs)
+        kc, vc = orc.reshape_and_cache(kc, vc, wl.new_key, wl.new_value, wl.slot_mapping)
+        per, n, el, thr = _cpu_timed(lambda: orc.decode(wl.q, kc, vc, wl.block_tables, wl.seq_lens,
+                                                        wl.scale), args.cpu_seconds)
+        cpu = {"value": round(logical / per / 1e9, 3), "unit": "GB/s (logical KV)", "cores": thr,
+               "kind": "oracle", "seconds_per_call": round(per, 4),
+               "sample": f"fp64 decode of all {wl.B} sequences (every sequence reads its own "
+                         f"copy of the prompt), repeated {n}x, {el:.1f} s"}
+    unique_gbs = unique / (sh["mean"] * 1e-6) / 1e9
     print(json.dumps({
         "bench": "shared_prefix", "workload": W.CONFIG_NAMES[3], "replicas_rotated": R,
         "groups": int(len(groups)), "members": max_members, "shared_tokens": max_shared,
@@ -221,7 +247,12 @@ def _shared_prefix(torch, pa, W, dev, args):
         "shared_logical_GBps": round(logical / (sh["mean"] * 1e-6) / 1e9, 1),
         "shared_unique_GBps": round(unique / (sh["mean"] * 1e-6) / 1e9, 1),
         "plain_logical_GBps": round(logical / (pl["mean"] * 1e-6) / 1e9, 1),
-        "speedup_vs_pa_decode": round(pl["mean"] / sh["mean"], 3)}), flush=True)
+        "speedup_vs_pa_decode": round(pl["mean"] / sh["mean"], 3),
+        "roofline": {"bound": "hbm", "kernel": "pa_decode_shared (one launch + merge)",
+                     "achieved": round(unique_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(unique_gbs / HBM_PEAK_GBS, 4),
+                     "bytes": "unique KV bytes (each shared block once)"},
+        "cpu_baseline": cpu}), flush=True)
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -279,13 +310,35 @@ def _multi_query(torch, pa, W, dev, args):
 
         t = _per_call_us(torch, multi, reps, steps, args.warmup, stream)
         sec = t["mean"] * 1e-6
+        hbm_bound = max_q * wl.G <= 16            # one query tile per (sequence, KV head)
+        if hbm_bound:
+            roof = {"bound": "hbm", "achieved": round(kv / sec / 1e9, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(kv / sec / 1e9 / HBM_PEAK_GBS, 4)}
+        else:
+            roof = {"bound": "mfma", "achieved": round(flops / sec / 1e12, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        roof["kernel"] = "pa_decode_multi"
+        cpu = None
+        if not args.no_cpu_baseline:
+            from oracle import oracle as orc
+            kc, vc = orc.reshape_and_cache(wl.k_cache, wl.v_cache, wl.new_key, wl.new_value,
+                                           wl.slot_mapping)
+            per, nrep, el, thr = _cpu_timed(lambda: orc.decode_multi(
+                wl.q, kc, vc, wl.block_tables, wl.seq_lens, qs, wl.scale), args.cpu_seconds)
+            cpu = {"value": round(kv / per / 1e9, 3) if hbm_bound else round(flops / per / 1e12, 4),
+                   "unit": "GB/s" if hbm_bound else "TFLOP/s", "cores": thr, "kind": "oracle",
+                   "seconds_per_call": round(per, 3),
+                   "sample": f"fp64 causal multi-query attention of all {total_q} queries, "
+                             f"repeated {nrep}x, {el:.1f} s"}
         line = {"bench": "multi_query", "workload": name, "B": wl.B, "queries": total_q,
                 "max_q": max_q, "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "block_size": wl.block_size,
                 "seq_lens": [int(x) for x in wl.seq_lens] if wl.B <= 8 else "llama3-8b batch",
                 "replicas_rotated": R, "decode_multi_us": t, "kv_bytes": kv,
                 "kv_GBps": round(kv / sec / 1e9, 1), "kv_frac_of_hbm": round(kv / sec / 1e9 / HBM_PEAK_GBS, 4),
                 "flops": flops, "TFLOPs": round(flops / sec / 1e12, 1),
-                "mfma_frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+                "mfma_frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "roofline": roof, "cpu_baseline": cpu}
         print(json.dumps(line), flush=True)
         del reps
         torch.cuda.empty_cache()
