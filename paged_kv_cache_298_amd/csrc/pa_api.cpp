@@ -126,8 +126,19 @@ namespace {
 
 struct MultiWs {
     pa_internal::MultiPlan plan;
-    size_t ml, total;
+    size_t ml, total;        // the query-tile split's records (0: no split)
+    int32_t stream_g;        // > 0: query columns of the stream decomposition, if it applies
+    StreamWs sws;
 };
+
+// The stream decomposition serves batches whose queries fit one 16-column score tile per
+// (sequence, KV head), max_q x G <= 16, with stream_g = 4, 8 or 16 columns.
+int32_t multi_stream_g(int32_t B, int32_t max_q, int32_t Hq, int32_t Hkv, int32_t block_size,
+                       int32_t max_blocks) {
+    const int64_t cols = (int64_t)max_q * (Hq / Hkv);
+    if (cols > 16 || !stream_eligible(PA_BF16, B, Hkv, block_size, max_blocks)) return 0;
+    return cols <= 4 ? 4 : (cols <= 8 ? 8 : 16);
+}
 
 MultiWs multi_workspace(int32_t B, int32_t total_q, int32_t max_q, int32_t Hq, int32_t Hkv,
                         int32_t D, int32_t block_size, int32_t max_blocks) {
@@ -139,6 +150,10 @@ MultiWs multi_workspace(int32_t B, int32_t total_q, int32_t max_q, int32_t Hq, i
         w.ml = (rows * (size_t)D * sizeof(float) + 255) / 256 * 256;
         w.total = w.ml + rows * 2 * sizeof(float);
     }
+    w.stream_g = multi_stream_g(B, max_q, Hq, Hkv, block_size, max_blocks);
+    w.sws = stream_workspace(w.stream_g > 0 ? w.stream_g : 4, D);
+    // enough for either decomposition, so the size does not depend on the path setting
+    if (w.stream_g > 0 && w.sws.total > w.total) w.total = w.sws.total;
     return w;
 }
 
@@ -462,10 +477,11 @@ int32_t pa_decode_multi(float* out, const void* q, const void* k_cache, const vo
         return fail(PA_ERR_INVALID_ARG, "pa_decode_multi: misaligned pointer");
     const MultiWs mw = multi_workspace(B, total_q, max_q, Hq, Hkv, D, block_size, max_blocks);
     const pa_internal::MultiPlan& pl = mw.plan;
+    const int32_t stream_g = g_path == PA_PATH_PARTITION ? 0 : mw.stream_g;
     const int64_t items = (int64_t)Hkv * pl.n_tiles * pl.n_parts * B;
     if (items > 0x7fffffff)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode_multi: work items exceed the grid limit");
-    if (pl.n_parts > 1 && (total_q > 65535 || Hq > 65535))
+    if (stream_g == 0 && pl.n_parts > 1 && (total_q > 65535 || Hq > 65535))
         return fail(PA_ERR_UNSUPPORTED, "pa_decode_multi: %d queries of a split launch exceed 65535", total_q);
     if (mw.total > 0) {
         if (!workspace || workspace_bytes < mw.total)
@@ -498,6 +514,20 @@ int32_t pa_decode_multi(float* out, const void* q, const void* k_cache, const vo
     a.n_tiles = pl.n_tiles;
     a.part_tokens = pl.part_tokens;
     a.n_parts = pl.n_parts;
+    a.stream_g = stream_g;
+    a.rec_o = nullptr;
+    a.rec_ml = nullptr;
+    a.desc = nullptr;
+    a.meta = nullptr;
+    if (stream_g > 0) {
+        char* ws = static_cast<char*>(workspace);
+        a.rec_o = reinterpret_cast<float*>(ws);
+        a.rec_ml = reinterpret_cast<float*>(ws + mw.sws.ml);
+        a.desc = reinterpret_cast<int32_t*>(ws + mw.sws.desc);
+        a.meta = reinterpret_cast<int32_t*>(ws + mw.sws.meta);
+    }
+    a.stream_waves = g_stream_waves;
+    a.min_slice = g_min_slice;
     a.scale = scale;
     a.stream = stream;
     const char* err = "";

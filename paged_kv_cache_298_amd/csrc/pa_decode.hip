@@ -268,17 +268,22 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(Params p) {
 // the per-sequence prefix of group counts kept in LDS, then gathers its table entry.
 // SPLIT: blocks of 8 tokens, so a 16-token group spans two physical blocks; each group
 // then has two tile offsets (tokens 0-7 and 8-15) and K lanes / V loads pick theirs.
-template <int D, int G, int DEPTH, bool SPLIT>
+template <int D, int G, int DEPTH, bool SPLIT, bool MULTI>
 __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
     constexpr int ROW = D * 2;              // bytes per cached row
     constexpr int NQ = D / 32;              // 16-byte registers per ring item
     constexpr int WV = D / 8;               // bytes of a V row per lane per load (16 or 8)
     constexpr int EV = D / 16;              // bf16 elements per lane per V load
-    constexpr int NSET = (G + 3) / 4;       // head sets of 4
+    // head sets of 4, each head repeated over the 16 columns; MULTI: one set whose 16
+    // columns hold the G (4, 8 or 16) query columns, repeated 16 / G times
+    constexpr int NSET = MULTI ? 1 : (G + 3) / 4;
     constexpr int G4 = G < 4 ? G : 4;       // distinct heads in a set
     constexpr int U = DEPTH / 2;            // groups in flight ahead of the consumer
     static_assert(D == 64 || D == 128, "head size");
     static_assert(DEPTH >= 2 && DEPTH % 2 == 0, "ring holds whole groups (K and V)");
+    // MULTI: G counts query columns, token j of the sequence's last n (its queries) times
+    // the GK heads of the KV head (column h = j GK + head); a row with no queries is empty
+    const int GK = MULTI ? p.Hq / p.Hkv : G;
 
     extern __shared__ int lds_prefix[];
     int* Cs = lds_prefix;           // [B + 1] exclusive prefix of groups per sequence
@@ -298,6 +303,11 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
         if (bb < p.B) {
             int L = p.lens[bb];
             L = L < 0 ? 0 : (L > cap ? cap : L);
+            if constexpr (MULTI) {
+                int qs_, n_;
+                multi_rows(p, bb, L, &qs_, &n_);
+                L = n_ > 0 ? L : 0;
+            }
             Ls[bb] = L;
             loc += (L + 15) >> 4;
         }
@@ -331,8 +341,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
         p.meta[0] = T;
         p.meta[1] = nwe;
     }
-    // empty sequences: a zero row per query head
-    for (int bb = gw; bb < p.B; bb += p.nw) {
+    // empty sequences: a zero row per query head (MULTI: an empty row has no queries)
+    for (int bb = gw; bb < (MULTI ? 0 : p.B); bb += p.nw) {
         if (__builtin_amdgcn_readfirstlane(Ls[bb]) == 0) {
             float* o = p.out + (int64_t)bb * p.Hq * D;
             for (int i = lane; i < p.Hq * D; i += 64) o[i] = 0.f;
@@ -391,9 +401,26 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
     // cache so that no vector register enters the cursor's updates.
     typedef __attribute__((address_space(4))) const int32_t* const_i32p;
     const const_i32p slens = (const_i32p)(p.lens);
+    const const_i32p sqs = (const_i32p)(p.q_starts);
+    // MULTI: first query row and query count of sequence bb, clamped as multi_rows does
+    auto seq_queries = [&](int bb, int L, int* qs, int* n) {
+        int a = sqs[bb];
+        a = a < 0 ? 0 : (a > p.total_q ? p.total_q : a);
+        int m = sqs[bb + 1] - a;
+        m = m < 0 ? 0 : m;
+        m = min(m, min(L, p.max_q));
+        *qs = a;
+        *n = min(m, p.total_q - a);
+    };
     auto seq_len = [&](int bb) -> int {
-        const int L = slens[bb];
-        return L < 0 ? 0 : (L > cap ? cap : L);
+        int L = slens[bb];
+        L = L < 0 ? 0 : (L > cap ? cap : L);
+        if constexpr (MULTI) {
+            int qs_, n_;
+            seq_queries(bb, L, &qs_, &n_);
+            L = n_ > 0 ? L : 0;
+        }
+        return L;
     };
     const int row0 = __builtin_amdgcn_readlane(w_row, 0);
     int cb = row0 / p.Hkv;
@@ -401,6 +428,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
     int cj = __builtin_amdgcn_readlane(w_j, 0);
     int cL = seq_len(cb);
     int cn = (cL + 15) >> 4;
+    int cqs = 0, cnq = 0;            // MULTI: the current row's first query and query count
+    if constexpr (MULTI) seq_queries(cb, cL, &cqs, &cnq);
     if (lane == 0) p.desc[gw] = make_int4(cb, cg, s0 - cj, cn);
 
     const int r = lane >> 4;     // row group
@@ -410,10 +439,22 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
     auto load_q = [&](int row, u32x4_t (&dst)[NSET][NQ]) {
         const int bq = row / p.Hkv;
         const int gq = row - bq * p.Hkv;
+        int qs = 0, nq = 0;
+        if constexpr (MULTI) seq_queries(bq, seq_len(bq), &qs, &nq);
 #pragma unroll
         for (int s = 0; s < NSET; ++s) {
-            const int h = 4 * s + ((c & 3) % G4);
-            const char* qrow = p.q + ((int64_t)bq * p.Hq + gq * G + h) * ROW;
+            const int h = MULTI ? c % G : 4 * s + ((c & 3) % G4);
+            const char* qrow;
+            if constexpr (MULTI) {
+                // column h = j GK + head; columns past the row's queries repeat its last
+                int j = h / GK;
+                j = j < nq ? j : nq - 1;
+                j = j < 0 ? 0 : j;
+                if (nq == 0) qs = 0;        // not reached for a row in the stream
+                qrow = p.q + ((int64_t)(qs + j) * p.Hq + gq * GK + (h - (h / GK) * GK)) * ROW;
+            } else {
+                qrow = p.q + ((int64_t)bq * p.Hq + gq * G + h) * ROW;
+            }
 #pragma unroll
             for (int k = 0; k < NQ; ++k)
                 dst[s][k] = *reinterpret_cast<const u32x4_t*>(qrow + (k * 32 + r * 8) * 2);
@@ -528,20 +569,28 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
             l_run[s] = rows_sum(l_run[s]);   // the output tile needs no sum: rows repeat
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                lh[s][m] = quad_bcast(l_run[s], m);
-                mh[s][m] = quad_bcast(m_run[s], m);
+                // output row 4r + m holds column 4r + m's query (MULTI), else head m
+                lh[s][m] = MULTI ? __shfl(l_run[s], 4 * r + m) : quad_bcast(l_run[s], m);
+                mh[s][m] = MULTI ? __shfl(m_run[s], 4 * r + m) : quad_bcast(m_run[s], m);
             }
         }
-        if (r == 0) {
+        // the row groups holding distinct outputs: one (rows repeat the heads), MULTI G / 4
+        if (MULTI ? 4 * r < G : r == 0) {
             const int rec = 2 * gw + (first_seg ? 0 : 1);
 #pragma unroll
             for (int s = 0; s < NSET; ++s) {
 #pragma unroll
                 for (int m = 0; m < G4; ++m) {
-                    const int h = 4 * s + m;
+                    const int h = MULTI ? 4 * r + m : 4 * s + m;
                     if (whole) {
                         const float inv = 1.0f / lh[s][m];
-                        float* dst = p.out + ((int64_t)cb * p.Hq + cg * G + h) * D + c * EV;
+                        int64_t orow = (int64_t)cb * p.Hq + cg * G + h;
+                        if constexpr (MULTI) {
+                            const int j = h / GK;
+                            if (j >= cnq) continue;          // no such query in this row
+                            orow = (int64_t)(cqs + j) * p.Hq + cg * GK + (h - j * GK);
+                        }
+                        float* dst = p.out + orow * D + c * EV;
 #pragma unroll
                         for (int e = 0; e < EV; e += 4)
                             *reinterpret_cast<float4*>(dst + e) =
@@ -605,13 +654,28 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) y[s][i] = (r + 4 * i < valid) ? y[s][i] : -INFINITY;
                     }
+                    if constexpr (MULTI) {
+                        // causal: column h (query j = h / GK) sees tokens up to L - n + j
+                        const int first_q = cL - cnq;
+                        if (16 * cj + 15 > first_q) {
+                            const int pos = first_q + (MULTI ? c % G : 4 * s + ((c & 3) % G4)) / GK;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                y[s][i] = (16 * cj + r + 4 * i <= pos) ? y[s][i] : -INFINITY;
+                        }
+                    }
                     const float mx = fmaxf(fmaxf(y[s][0], y[s][1]), fmaxf(y[s][2], y[s][3]));
-                    const float m_new = fmaxf(m_run[s], rows_max(mx));
-                    const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_new);
+                    float m_new = fmaxf(m_run[s], rows_max(mx));
+                    // MULTI: a column may see no token of a segment (its query comes before
+                    // the segment): 0 as the reference keeps its factors 0 instead of NaN
+                    float m_ref = m_new;
+                    if constexpr (MULTI) m_ref = m_new == -INFINITY ? 0.f : m_new;
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_ref);
                     m_run[s] = m_new;
                     float am[4];
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) am[m] = quad_bcast(alpha, m);
+                    for (int m = 0; m < 4; ++m)
+                        am[m] = MULTI ? __shfl(alpha, 4 * r + m) : quad_bcast(alpha, m);
 #pragma unroll
                     for (int e = 0; e < EV; ++e)
 #pragma unroll
@@ -619,9 +683,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
                     // probabilities, rounded to bf16 for the matrix cores; the sum takes
                     // the rounded values too, so the weights it divides by are the ones used
                     const bf16x2_t p01 = __builtin_convertvector(
-                        (f32x2_t){__builtin_amdgcn_exp2f(y[s][0] - m_new), __builtin_amdgcn_exp2f(y[s][1] - m_new)}, bf16x2_t);
+                        (f32x2_t){__builtin_amdgcn_exp2f(y[s][0] - m_ref), __builtin_amdgcn_exp2f(y[s][1] - m_ref)}, bf16x2_t);
                     const bf16x2_t p23 = __builtin_convertvector(
-                        (f32x2_t){__builtin_amdgcn_exp2f(y[s][2] - m_new), __builtin_amdgcn_exp2f(y[s][3] - m_new)}, bf16x2_t);
+                        (f32x2_t){__builtin_amdgcn_exp2f(y[s][2] - m_ref), __builtin_amdgcn_exp2f(y[s][3] - m_ref)}, bf16x2_t);
                     pw[s][0] = __builtin_bit_cast(uint32_t, p01);
                     pw[s][1] = __builtin_bit_cast(uint32_t, p23);
                     l_run[s] = l_run[s] * alpha + ((lo_bf16(pw[s][0]) + hi_bf16(pw[s][0])) +
@@ -679,6 +743,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
                             } while (cL == 0 && cb < p.B - 1);
                         }
                         cn = (cL + 15) >> 4;
+                        if constexpr (MULTI) seq_queries(cb, cL, &cqs, &cnq);
                         seg_j0 = 0;
                         first_seg = false;
                         const int row = cb * p.Hkv + cg;
@@ -710,7 +775,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
 // slice w - 1, so every split row is merged exactly once, records in slice order. The
 // merge is latency-bound: one thread per float4 of the row's G x D output, the header
 // and the descriptor fetched together, and a row's records loaded kBatch at a time.
-template <int D, int G>
+template <int D, int G, bool MULTI>
 __global__ __launch_bounds__(G * D / 4 < 64 ? 64 : G * D / 4) void stream_reduce_kernel(Params p) {
     constexpr int C4 = D / 4;
     constexpr int kBatch = 8;
@@ -760,7 +825,20 @@ __global__ __launch_bounds__(G * D / 4 < 64 ? 64 : G * D / 4) void stream_reduce
         M = Mb;
     }
     const float inv = 1.0f / l;
-    reinterpret_cast<float4*>(p.out + ((int64_t)d.x * p.Hq + d.y * G + h) * D)[c4] =
+    int64_t orow = (int64_t)d.x * p.Hq + d.y * G + h;
+    if constexpr (MULTI) {
+        // column h is query j = h / GK of the row's sequence (none past its query count)
+        const int GK = p.Hq / p.Hkv;
+        const int cap = p.max_blocks * p.bs;
+        int L = p.lens[d.x];
+        L = L < 0 ? 0 : (L > cap ? cap : L);
+        int qs, n;
+        multi_rows(p, d.x, L, &qs, &n);
+        const int j = h / GK;
+        if (j >= n) return;
+        orow = (int64_t)(qs + j) * p.Hq + d.y * GK + (h - j * GK);
+    }
+    reinterpret_cast<float4*>(p.out + orow * D)[c4] =
         make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
 }
 
@@ -822,7 +900,7 @@ int stream_shape(size_t need_lds, int* nw, size_t* lds) {
     return 0;
 }
 
-template <int D, int G, bool SPLIT>
+template <int D, int G, bool SPLIT, bool MULTI = false>
 hipError_t launch_stream(Params prm, int nw_req, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     size_t lds = (size_t)(2 * prm.B + 1) * sizeof(int);
@@ -834,9 +912,9 @@ hipError_t launch_stream(Params prm, int nw_req, void* stream) {
     nw = nw > pa_internal::kMaxStreamWaves ? pa_internal::kMaxStreamWaves : nw;
     nw = (nw + 3) / 4 * 4;
     prm.nw = nw;
-    hipLaunchKernelGGL((decode_stream_kernel<D, G, PA_STREAM_DEPTH, SPLIT>), dim3(nw / 4), dim3(256), lds, s, prm);
+    hipLaunchKernelGGL((decode_stream_kernel<D, G, PA_STREAM_DEPTH, SPLIT, MULTI>), dim3(nw / 4), dim3(256), lds, s, prm);
     constexpr int kMergeThreads = G * D / 4 < 64 ? 64 : G * D / 4;
-    hipLaunchKernelGGL((stream_reduce_kernel<D, G>), dim3(nw), dim3(kMergeThreads), 0, s, prm);
+    hipLaunchKernelGGL((stream_reduce_kernel<D, G, MULTI>), dim3(nw), dim3(kMergeThreads), 0, s, prm);
     return hipGetLastError();
 }
 
@@ -915,6 +993,50 @@ int launch_decode(const DecodeLaunch& a, const char** err) {
     } else {
         e = a.kv_dtype == 1 ? dispatch_d<true>(prm, a.B, a.Hkv, a.D, G, a.stream)
                             : dispatch_d<false>(prm, a.B, a.Hkv, a.D, G, a.stream);
+    }
+    if (e != hipSuccess) {
+        *err = hipGetErrorString(e);
+        return (int)e;
+    }
+    return 0;
+}
+
+int launch_multi_stream(const MultiLaunch& a, const char** err) {
+    Params prm{};
+    prm.out = a.out;
+    prm.q = static_cast<const char*>(a.q);
+    prm.k = static_cast<const char*>(a.k);
+    prm.v = static_cast<const char*>(a.v);
+    prm.tables = a.tables;
+    prm.lens = a.lens;
+    prm.B = a.B;
+    prm.Hq = a.Hq;
+    prm.Hkv = a.Hkv;
+    prm.bs = a.bs;
+    int shift = 0;
+    while ((1 << shift) < a.bs) ++shift;
+    prm.bs_shift = shift;
+    prm.num_blocks = a.num_blocks;
+    prm.max_blocks = a.max_blocks;
+    prm.scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+    prm.rec_o = a.rec_o;
+    prm.rec_ml = reinterpret_cast<float2*>(a.rec_ml);
+    prm.desc = reinterpret_cast<int4*>(a.desc);
+    prm.meta = a.meta;
+    prm.min_slice = a.min_slice > 0 ? a.min_slice : 1;
+    prm.q_starts = a.q_starts;
+    prm.total_q = a.total_q;
+    prm.max_q = a.max_q;
+    if (a.B == 0 || a.total_q == 0) return 0;
+    hipError_t e = hipErrorInvalidValue;
+    if (a.D == 64) {
+        if (a.stream_g == 4) e = launch_stream<64, 4, false, true>(prm, a.stream_waves, a.stream);
+        else if (a.stream_g == 8) e = launch_stream<64, 8, false, true>(prm, a.stream_waves, a.stream);
+        else if (a.stream_g == 16) e = launch_stream<64, 16, false, true>(prm, a.stream_waves, a.stream);
+    } else if (a.D == 128) {
+        if (a.stream_g == 4) e = launch_stream<128, 4, false, true>(prm, a.stream_waves, a.stream);
+        else if (a.stream_g == 8) e = launch_stream<128, 8, false, true>(prm, a.stream_waves, a.stream);
+        else if (a.stream_g == 16) e = launch_stream<128, 16, false, true>(prm, a.stream_waves, a.stream);
     }
     if (e != hipSuccess) {
         *err = hipGetErrorString(e);

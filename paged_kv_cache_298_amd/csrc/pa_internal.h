@@ -81,6 +81,14 @@ struct MultiLaunch {
     int32_t B, total_q, max_q, Hq, Hkv, D, bs, num_blocks, max_blocks;
     int32_t nset;            // query tile = 16 nset rows
     int32_t n_tiles, part_tokens, n_parts;
+    // stream decomposition (stream_g > 0): the decode kernel's slices with stream_g query
+    // columns (token x head) per row instead of query tiles
+    int32_t stream_g;
+    float* rec_o;
+    float* rec_ml;
+    int32_t* desc;
+    int32_t* meta;
+    int32_t stream_waves, min_slice;
     float scale;
     void* stream;
 };
@@ -107,6 +115,7 @@ constexpr int kMultiMinPart = PA_MULTI_MIN_PART;     // ... but not below this m
 int launch_decode(const DecodeLaunch& a, const char** err);
 int launch_decode_shared(const SharedLaunch& a, const char** err);
 int launch_decode_multi(const MultiLaunch& a, const char** err);
+int launch_multi_stream(const MultiLaunch& a, const char** err);   // stream_g > 0
 int launch_reshape_and_cache(void* k_cache, void* v_cache, const void* key, const void* value,
                              const int32_t* slot_mapping, int32_t T, int32_t Hkv,
                              int32_t row_bytes, int32_t block_size, int32_t num_blocks,

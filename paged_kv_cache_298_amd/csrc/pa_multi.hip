@@ -676,6 +676,7 @@ int launch_decode_shared(const SharedLaunch& a, const char** err) {
 }
 
 int launch_decode_multi(const MultiLaunch& a, const char** err) {
+    if (a.stream_g > 0) return launch_multi_stream(a, err);
     Params prm{};
     prm.out = a.out;
     prm.ws_o = a.ws_o;

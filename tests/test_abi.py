@@ -255,10 +255,14 @@ def test_decode_multi_rejects_bad_arguments(kw, status):
 def test_decode_multi_workspace_and_empty_batch():
     assert _multi(B=0, out=None, q=None) == pa.PA_OK
     assert _multi(tq=0, out=None, q=None) == pa.PA_OK
-    # four draft tokens on 64 sequences of up to 4096 tokens: 64 x 8 units, split into 4
-    # partitions of 1024 tokens; records [256 queries x 32 heads x 4, D] plus (m, l)
+    # four draft tokens on 64 sequences of up to 4096 tokens: the query-tile split has 4
+    # partitions of 1024 tokens, records [256 queries x 32 heads x 4, D] plus (m, l); the
+    # stream decomposition (4 x 4 = 16 query columns) needs records for 2 x 4096 slices
     rows = 256 * 32 * 4
-    assert pa.pa_decode_multi_workspace_bytes(64, 256, 4, 32, 8, 128, 16, 256) == _up(rows * 128 * 4) + rows * 8
-    # 1024-token chunks of 4 sequences: 64 tiles each, enough items without a split
+    tiles = _up(rows * 128 * 4) + rows * 8
+    stream = _up(_up(_up(8192 * 16 * 128 * 4) + 8192 * 16 * 8) + 4096 * 16) + 16
+    assert pa.pa_decode_multi_workspace_bytes(64, 256, 4, 32, 8, 128, 16, 256) == max(tiles, stream)
+    # 1024-token chunks of 4 sequences: 64 tiles each, enough items without a split, and
+    # too many columns for the stream decomposition
     assert pa.pa_decode_multi_workspace_bytes(4, 4096, 1024, 32, 8, 128, 16, 256) == 0
     assert pa.pa_decode_multi_workspace_bytes(0, 4, 4, 32, 8, 128, 16, 256) == 0

@@ -157,3 +157,42 @@ def test_loose_max_q_bound_and_empty_chunks(pa, oracle):
     torch.cuda.synchronize()
     ref = _multi_oracle(oracle, wl)
     assert max_err(out.cpu().numpy(), ref) <= TOL[W.BF16]
+
+
+# ------------------------------------------------ the stream decomposition (<= 16 columns)
+
+STREAM = [
+    # name, lens, n_new, Hq, Hkv, D, bs   (max n x G <= 16: one score tile per row)
+    ("g4-n4", [300, 1, 77, 1000, 17, 640], [4, 1, 3, 4, 0, 2], 32, 8, 128, 16),
+    ("g8-n2", [500, 33, 900], [2, 1, 2], 64, 8, 128, 32),
+    ("g2-n3", [129, 400, 3, 64], [3, 3, 3, 1], 16, 8, 128, 16),    # 6 of 8 columns used
+    ("g1-n16", [700, 16, 300], [16, 16, 5], 8, 8, 64, 64),
+]
+
+
+@pytest.mark.parametrize("waves", [0, 96], ids=["all-waves", "96-waves"])
+@pytest.mark.parametrize("case", STREAM, ids=lambda c: c[0])
+def test_stream_decomposition_matches_oracle(pa, oracle, case, waves):
+    """Draft-sized chunks go through the decode kernel's slices (equal groups per wave,
+    rows split across waves and merged); with 96 waves most rows are split."""
+    name, lens, n_new, Hq, Hkv, D, bs = case
+    wl = W.make_workload(f"mqs-{name}", len(lens), Hq, Hkv, D, bs, lens, W.BF16,
+                         seed=sum(lens) + 3 * bs, n_new=n_new)
+    pa.pa_set_stream_waves(waves, 1 if waves else 0)
+    try:
+        _parity(pa, oracle, wl, f"stream {name} waves={waves}")
+    finally:
+        pa.pa_set_stream_waves(0, 0)
+
+
+def test_stream_and_tile_decompositions_agree(pa):
+    rng = np.random.default_rng(12)
+    lens = rng.integers(4, 2000, size=24)
+    wl = W.make_workload("mqs-agree", 24, 32, 8, 128, 16, lens, W.BF16, seed=12, n_new=[4] * 24)
+    (a,), _ = _multi_gpu(pa, wl)
+    pa.pa_set_decode_path(pa.PA_PATH_PARTITION)        # query tiles instead
+    try:
+        (b,), _ = _multi_gpu(pa, wl)
+    finally:
+        pa.pa_set_decode_path(pa.PA_PATH_AUTO)
+    assert max_err(a, b) <= TOL[W.BF16]
