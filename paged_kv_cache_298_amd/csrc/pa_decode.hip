@@ -268,15 +268,18 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(Params p) {
 // the per-sequence prefix of group counts kept in LDS, then gathers its table entry.
 // SPLIT: blocks of 8 tokens, so a 16-token group spans two physical blocks; each group
 // then has two tile offsets (tokens 0-7 and 8-15) and K lanes / V loads pick theirs.
-template <int D, int G, int DEPTH, bool SPLIT, bool MULTI>
+template <int D, int G, int DEPTH, bool SPLIT, bool MULTI, bool DIST>
 __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
     constexpr int ROW = D * 2;              // bytes per cached row
     constexpr int NQ = D / 32;              // 16-byte registers per ring item
     constexpr int WV = D / 8;               // bytes of a V row per lane per load (16 or 8)
     constexpr int EV = D / 16;              // bf16 elements per lane per V load
-    // head sets of 4, each head repeated over the 16 columns; MULTI: one set whose 16
-    // columns hold the G (4, 8 or 16) query columns, repeated 16 / G times
-    constexpr int NSET = MULTI ? 1 : (G + 3) / 4;
+    // head sets of 4, each head repeated over the 16 columns; COLS (MULTI, or DIST for a
+    // decode with G = 8): one set whose 16 columns hold the G (4, 8 or 16) query columns,
+    // repeated 16 / G times, so that output row 4r + i of the PV tile is column 4r + i
+    constexpr bool COLS = MULTI || DIST;
+    static_assert(!COLS || G == 4 || G == 8 || G == 16, "columns of one tile");
+    constexpr int NSET = COLS ? 1 : (G + 3) / 4;
     constexpr int G4 = G < 4 ? G : 4;       // distinct heads in a set
     constexpr int U = DEPTH / 2;            // groups in flight ahead of the consumer
     static_assert(D == 64 || D == 128, "head size");
@@ -443,7 +446,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
         if constexpr (MULTI) seq_queries(bq, seq_len(bq), &qs, &nq);
 #pragma unroll
         for (int s = 0; s < NSET; ++s) {
-            const int h = MULTI ? c % G : 4 * s + ((c & 3) % G4);
+            const int h = COLS ? c % G : 4 * s + ((c & 3) % G4);
             const char* qrow;
             if constexpr (MULTI) {
                 // column h = j GK + head; columns past the row's queries repeat its last
@@ -569,19 +572,19 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
             l_run[s] = rows_sum(l_run[s]);   // the output tile needs no sum: rows repeat
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                // output row 4r + m holds column 4r + m's query (MULTI), else head m
-                lh[s][m] = MULTI ? __shfl(l_run[s], 4 * r + m) : quad_bcast(l_run[s], m);
-                mh[s][m] = MULTI ? __shfl(m_run[s], 4 * r + m) : quad_bcast(m_run[s], m);
+                // output row 4r + m holds column 4r + m (COLS), else head m
+                lh[s][m] = COLS ? __shfl(l_run[s], 4 * r + m) : quad_bcast(l_run[s], m);
+                mh[s][m] = COLS ? __shfl(m_run[s], 4 * r + m) : quad_bcast(m_run[s], m);
             }
         }
-        // the row groups holding distinct outputs: one (rows repeat the heads), MULTI G / 4
-        if (MULTI ? 4 * r < G : r == 0) {
+        // the row groups holding distinct outputs: one (rows repeat the heads), COLS G / 4
+        if (COLS ? 4 * r < G : r == 0) {
             const int rec = 2 * gw + (first_seg ? 0 : 1);
 #pragma unroll
             for (int s = 0; s < NSET; ++s) {
 #pragma unroll
                 for (int m = 0; m < G4; ++m) {
-                    const int h = MULTI ? 4 * r + m : 4 * s + m;
+                    const int h = COLS ? 4 * r + m : 4 * s + m;
                     if (whole) {
                         const float inv = 1.0f / lh[s][m];
                         int64_t orow = (int64_t)cb * p.Hq + cg * G + h;
@@ -658,7 +661,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
                         // causal: column h (query j = h / GK) sees tokens up to L - n + j
                         const int first_q = cL - cnq;
                         if (16 * cj + 15 > first_q) {
-                            const int pos = first_q + (MULTI ? c % G : 4 * s + ((c & 3) % G4)) / GK;
+                            const int pos = first_q + (c % G) / GK;
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
                                 y[s][i] = (16 * cj + r + 4 * i <= pos) ? y[s][i] : -INFINITY;
@@ -675,7 +678,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
                     float am[4];
 #pragma unroll
                     for (int m = 0; m < 4; ++m)
-                        am[m] = MULTI ? __shfl(alpha, 4 * r + m) : quad_bcast(alpha, m);
+                        am[m] = COLS ? __shfl(alpha, 4 * r + m) : quad_bcast(alpha, m);
 #pragma unroll
                     for (int e = 0; e < EV; ++e)
 #pragma unroll
@@ -900,7 +903,7 @@ int stream_shape(size_t need_lds, int* nw, size_t* lds) {
     return 0;
 }
 
-template <int D, int G, bool SPLIT, bool MULTI = false>
+template <int D, int G, bool SPLIT, bool MULTI = false, bool DIST = false>
 hipError_t launch_stream(Params prm, int nw_req, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     size_t lds = (size_t)(2 * prm.B + 1) * sizeof(int);
@@ -912,7 +915,7 @@ hipError_t launch_stream(Params prm, int nw_req, void* stream) {
     nw = nw > pa_internal::kMaxStreamWaves ? pa_internal::kMaxStreamWaves : nw;
     nw = (nw + 3) / 4 * 4;
     prm.nw = nw;
-    hipLaunchKernelGGL((decode_stream_kernel<D, G, PA_STREAM_DEPTH, SPLIT, MULTI>), dim3(nw / 4), dim3(256), lds, s, prm);
+    hipLaunchKernelGGL((decode_stream_kernel<D, G, PA_STREAM_DEPTH, SPLIT, MULTI, DIST>), dim3(nw / 4), dim3(256), lds, s, prm);
     constexpr int kMergeThreads = G * D / 4 < 64 ? 64 : G * D / 4;
     hipLaunchKernelGGL((stream_reduce_kernel<D, G, MULTI>), dim3(nw), dim3(kMergeThreads), 0, s, prm);
     return hipGetLastError();
@@ -924,7 +927,7 @@ hipError_t dispatch_stream_g(const Params& prm, int G, int nw, void* stream) {
         case 1: return launch_stream<D, 1, SPLIT>(prm, nw, stream);
         case 2: return launch_stream<D, 2, SPLIT>(prm, nw, stream);
         case 4: return launch_stream<D, 4, SPLIT>(prm, nw, stream);
-        case 8: return launch_stream<D, 8, SPLIT>(prm, nw, stream);
+        case 8: return launch_stream<D, 8, SPLIT, false, (PA_STREAM_DIST8 != 0)>(prm, nw, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -35,6 +35,11 @@
 #ifndef PA_STREAM_DEPTH
 #define PA_STREAM_DEPTH 4
 #endif
+// G = 8 decode in the stream kernel: one set of 8 distinct head columns (repeated twice)
+// rather than two sets of 4 heads repeated four times (half the matrix and softmax work)
+#ifndef PA_STREAM_DIST8
+#define PA_STREAM_DIST8 1
+#endif
 #ifndef PA_DECODE_DEPTH
 #define PA_DECODE_DEPTH 4
 #endif
