@@ -516,7 +516,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
         }
 #pragma unroll
         for (int k = 0; k < NQ; ++k)
-            dst.q[k] = *reinterpret_cast<const u32x4_t*>(kb + koff + k * 64);
+            dst.q[k] = kv_load16(reinterpret_cast<const u32x4_t*>(kb + koff + k * 64));
     };
     // V load k holds rows r + 4k; with SPLIT, loads 2 and 3 (rows 8-15) read the second
     // block at rows r + 4 (k - 2)
@@ -531,7 +531,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
         if constexpr (WV == 16) {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                dst.q[k] = *reinterpret_cast<const u32x4_t*>(vaddr(k));
+                dst.q[k] = kv_load16(reinterpret_cast<const u32x4_t*>(vaddr(k)));
         } else {
 #pragma unroll
             for (int k = 0; k < 4; k += 2) {
