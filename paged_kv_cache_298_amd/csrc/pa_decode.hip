@@ -773,16 +773,27 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
     }
 }
 
-// Merge the partial records of rows that cross slice boundaries. Group w looks at the
+// Merge the partial records of rows that cross slice boundaries. Workgroup w looks at the
 // row holding the first group of slice w; it merges it only when that row began inside
-// slice w - 1, so every split row is merged exactly once, records in slice order. The
-// merge is latency-bound: one thread per float4 of the row's G x D output, the header
-// and the descriptor fetched together, and a row's records loaded kBatch at a time.
+// slice w - 1, so every split row is merged exactly once. The merge is latency-bound, so
+// the row's records (one per slice it touches, up to ~50 for the longest rows) are dealt
+// to the four waves in contiguous runs: each wave loads its run up to kBatch records at a
+// time, each lane holding F float4 of the row's G x D output, and keeps a running state;
+// the four states are then combined through LDS in wave order. The header and the
+// descriptor are fetched together. The order of every sum is fixed, so results repeat
+// bitwise.
 template <int D, int G, bool MULTI>
-__global__ __launch_bounds__(G * D / 4 < 64 ? 64 : G * D / 4) void stream_reduce_kernel(Params p) {
+__global__ __launch_bounds__(256) void stream_reduce_kernel(Params p) {
     constexpr int C4 = D / 4;
-    constexpr int kBatch = 8;
+    constexpr int NF = G * C4;            // float4s of a row's output
+    constexpr int F = (NF + 63) / 64;     // float4s per lane
+    constexpr int kBatch = F >= 4 ? 4 : 16 / F;   // records per round trip
+    __shared__ float4 s_o[4][NF];
+    __shared__ float2 s_ml[4][NF];
+    const int lane = threadIdx.x & 63;
+    const int wid = threadIdx.x >> 6;
     const int w = blockIdx.x;
+    if (w >= p.nw) return;
     const int T = p.meta[0];
     const int nwe = p.meta[1];
     const int4 d = p.desc[w];          // b, g, row start, row groups
@@ -791,58 +802,118 @@ __global__ __launch_bounds__(G * D / 4 < 64 ? 64 : G * D / 4) void stream_reduce
     if (d.z >= s0w) return;            // the row starts in slice w: not split here
     const int s0p = (int)((int64_t)(w - 1) * T / nwe);
     if (d.z < s0p) return;             // began before slice w - 1: merged by an earlier group
-    const int i = threadIdx.x;
-    if (i >= G * C4) return;
-    const int h = i / C4, c4 = i % C4;
     const int last = d.z + d.w - 1;
     const int wb = (int)(((int64_t)(last + 1) * nwe - 1) / T);   // slice holding the last group
     const int nrec = wb - w + 2;       // slices w - 1 .. wb
     const int rec_a = 2 * (w - 1) + (d.z == s0p ? 0 : 1);
-    float M = -INFINITY, l = 0.f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int x0 = 0; x0 < nrec; x0 += kBatch) {   // running merge in slice order
-        float2 ml[kBatch];
-        float4 v[kBatch];
+    // this wave's run of records [xa, xb)
+    const int per = (nrec + 3) >> 2;
+    const int xa = min(nrec, wid * per);
+    const int xb = min(nrec, xa + per);
+    int hh[F], cc[F];                  // head and float4 column of each of the lane's float4s
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+        int i = lane + 64 * f;
+        i = i < NF ? i : NF - 1;
+        hh[f] = i / C4;
+        cc[f] = i - hh[f] * C4;
+    }
+    float M[F], l[F];
+    float4 o[F];
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+        M[f] = -INFINITY;
+        l[f] = 0.f;
+        o[f] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int x0 = xa; x0 < xb; x0 += kBatch) {   // running merge in slice order
+        float2 ml[kBatch][F];
+        float4 v[kBatch][F];
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
-            const int x = x0 + k < nrec ? x0 + k : nrec - 1;
-            const int rec = x == 0 ? rec_a : 2 * (w - 1 + x);
-            ml[k] = p.rec_ml[(int64_t)rec * G + h];
-            v[k] = reinterpret_cast<const float4*>(p.rec_o + ((int64_t)rec * G + h) * D)[c4];
-        }
-        float Mb = M;
+            if (x0 + k < xb) {         // wave-uniform: no load for a record past the run
+                const int x = x0 + k;
+                const int rec = x == 0 ? rec_a : 2 * (w - 1 + x);
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k)
-            if (x0 + k < nrec) Mb = fmaxf(Mb, ml[k].x);
-        const float a = __builtin_amdgcn_exp2f(M - Mb);   // 0 on the first batch
-        o.x *= a; o.y *= a; o.z *= a; o.w *= a;
-        l *= a;
+                for (int f = 0; f < F; ++f) {
+                    ml[k][f] = p.rec_ml[(int64_t)rec * G + hh[f]];
+                    v[k][f] = reinterpret_cast<const float4*>(p.rec_o + ((int64_t)rec * G + hh[f]) * D)[cc[f]];
+                }
+            } else {
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            if (x0 + k < nrec) {
-                const float wgt = __builtin_amdgcn_exp2f(ml[k].x - Mb);
-                o.x += wgt * v[k].x; o.y += wgt * v[k].y; o.z += wgt * v[k].z; o.w += wgt * v[k].w;
-                l += wgt * ml[k].y;
+                for (int f = 0; f < F; ++f) {
+                    ml[k][f] = make_float2(-INFINITY, 0.f);
+                    v[k][f] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
             }
         }
-        M = Mb;
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+            float Mb = M[f];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) Mb = fmaxf(Mb, ml[k][f].x);
+            // a multi-query column may see no token of a whole run: 0 as the reference
+            // keeps its factors 0 instead of NaN
+            const float Mr = Mb == -INFINITY ? 0.f : Mb;
+            const float a = __builtin_amdgcn_exp2f(M[f] - Mr);   // 0 on the first batch
+            o[f].x *= a; o[f].y *= a; o[f].z *= a; o[f].w *= a;
+            l[f] *= a;
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const float wgt = __builtin_amdgcn_exp2f(ml[k][f].x - Mr);   // 0 past the run
+                o[f].x += wgt * v[k][f].x; o[f].y += wgt * v[k][f].y;
+                o[f].z += wgt * v[k][f].z; o[f].w += wgt * v[k][f].w;
+                l[f] += wgt * ml[k][f].y;
+            }
+            M[f] = Mb;
+        }
     }
-    const float inv = 1.0f / l;
-    int64_t orow = (int64_t)d.x * p.Hq + d.y * G + h;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+        const int i = lane + 64 * f;
+        if (i < NF) {
+            s_o[wid][i] = o[f];
+            s_ml[wid][i] = make_float2(M[f], l[f]);
+        }
+    }
+    __syncthreads();
+    int qs = 0, n = 0;
     if constexpr (MULTI) {
-        // column h is query j = h / GK of the row's sequence (none past its query count)
-        const int GK = p.Hq / p.Hkv;
         const int cap = p.max_blocks * p.bs;
         int L = p.lens[d.x];
         L = L < 0 ? 0 : (L > cap ? cap : L);
-        int qs, n;
         multi_rows(p, d.x, L, &qs, &n);
-        const int j = h / GK;
-        if (j >= n) return;
-        orow = (int64_t)(qs + j) * p.Hq + d.y * GK + (h - j * GK);
     }
-    reinterpret_cast<float4*>(p.out + orow * D)[c4] =
-        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    // the four states in wave order; wave 0 holds the row's first record, whose maximum is
+    // finite for every column, so Mx is finite and an empty run weighs 0
+    for (int i = threadIdx.x; i < NF; i += 256) {
+        float2 mlq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mlq[q] = s_ml[q][i];
+        const float Mx = fmaxf(fmaxf(mlq[0].x, mlq[1].x), fmaxf(mlq[2].x, mlq[3].x));
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        float lsum = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float wgt = __builtin_amdgcn_exp2f(mlq[q].x - Mx);
+            const float4 oq = s_o[q][i];
+            acc.x += wgt * oq.x; acc.y += wgt * oq.y; acc.z += wgt * oq.z; acc.w += wgt * oq.w;
+            lsum += wgt * mlq[q].y;
+        }
+        const int h = i / C4;
+        const int c4 = i - h * C4;
+        int64_t orow = (int64_t)d.x * p.Hq + d.y * G + h;
+        if constexpr (MULTI) {
+            // column h is query j = h / GK of the row's sequence (none past its query count)
+            const int GK = p.Hq / p.Hkv;
+            const int j = h / GK;
+            if (j >= n) continue;
+            orow = (int64_t)(qs + j) * p.Hq + d.y * GK + (h - j * GK);
+        }
+        const float inv = 1.0f / lsum;
+        reinterpret_cast<float4*>(p.out + orow * D)[c4] =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
 }
 
 template <bool BF16, int D, int G>
@@ -916,8 +987,7 @@ hipError_t launch_stream(Params prm, int nw_req, void* stream) {
     nw = (nw + 3) / 4 * 4;
     prm.nw = nw;
     hipLaunchKernelGGL((decode_stream_kernel<D, G, PA_STREAM_DEPTH, SPLIT, MULTI, DIST>), dim3(nw / 4), dim3(256), lds, s, prm);
-    constexpr int kMergeThreads = G * D / 4 < 64 ? 64 : G * D / 4;
-    hipLaunchKernelGGL((stream_reduce_kernel<D, G, MULTI>), dim3(nw), dim3(kMergeThreads), 0, s, prm);
+    hipLaunchKernelGGL((stream_reduce_kernel<D, G, MULTI>), dim3(nw), dim3(256), 0, s, prm);
     return hipGetLastError();
 }
 

@@ -209,6 +209,20 @@ __device__ __forceinline__ u32x4_t kv_load16(const u32x4_t* ptr) {
 #endif
 }
 
+// Non-temporal K/V loads of the bf16 partition item (partition decode, shared-prefix
+// suffixes) and of the shared-prefix tiles, each read once per call.
+#ifndef PA_ITEM_NT
+#define PA_ITEM_NT 1
+#endif
+#ifndef PA_PREFIX_NT
+#define PA_PREFIX_NT 1
+#endif
+template <bool NT>
+__device__ __forceinline__ u32x4_t ld16(const u32x4_t* ptr) {
+    if constexpr (NT) return __builtin_nontemporal_load(ptr);
+    else return *ptr;
+}
+
 // K/V bytes are read once per call: stream them past the caches when PA_DECODE_NT is set.
 __device__ __forceinline__ u32x4_t load16(const u32x4_t* ptr) {
 #if PA_DECODE_NT
@@ -438,13 +452,13 @@ __device__ __forceinline__ void bf16_item(const Params& p, int id) {
             const char* kb = kbase + off;
 #pragma unroll
             for (int k = 0; k < NQ; ++k)
-                dst.q[k] = *reinterpret_cast<const u32x4_t*>(kb + koff + k * 64);
+                dst.q[k] = ld16<PA_ITEM_NT != 0>(reinterpret_cast<const u32x4_t*>(kb + koff + k * 64));
         } else {
             const char* vb = vbase + off;
             if constexpr (WV == 16) {
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    dst.q[k] = *reinterpret_cast<const u32x4_t*>(vb + voff + k * 4 * ROW);
+                    dst.q[k] = ld16<PA_ITEM_NT != 0>(reinterpret_cast<const u32x4_t*>(vb + voff + k * 4 * ROW));
             } else {
 #pragma unroll
                 for (int k = 0; k < 4; k += 2) {

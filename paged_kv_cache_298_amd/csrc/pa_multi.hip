@@ -99,14 +99,14 @@ __device__ __forceinline__ void prefix_item(const Params& p, int id) {
     auto issue_k = [&](int gq, Item& dst) {
         const char* kb = kbase + goff(gq);
 #pragma unroll
-        for (int k = 0; k < NQ; ++k) dst.q[k] = *reinterpret_cast<const u32x4_t*>(kb + koff + k * 64);
+        for (int k = 0; k < NQ; ++k) dst.q[k] = ld16<PA_PREFIX_NT != 0>(reinterpret_cast<const u32x4_t*>(kb + koff + k * 64));
     };
     auto issue_v = [&](int gq, Item& dst) {
         const char* vb = vbase + goff(gq);
         if constexpr (WV == 16) {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                dst.q[k] = *reinterpret_cast<const u32x4_t*>(vb + voff + k * 4 * ROW);
+                dst.q[k] = ld16<PA_PREFIX_NT != 0>(reinterpret_cast<const u32x4_t*>(vb + voff + k * 4 * ROW));
         } else {
 #pragma unroll
             for (int k = 0; k < 4; k += 2) {
