@@ -2,7 +2,7 @@
 
 A step is the whole hot path over one batch: clone shared blocks (copy_blocks, when the
 workload has copy-on-write pairs), write each sequence's newest K/V (reshape_and_cache),
-then paged decode attention (pa_decode: partition kernel + split-sequence reduce). Inputs
+then paged decode attention (pa_decode: stream decode kernel + split-row merge). Inputs
 are seeded synthetic data resident in HBM before timing starts; successive steps rotate
 over R replicas of (pool, q, tables, ...) so the working set exceeds the 256 MB Infinity
 Cache. Prints ONE JSON line.
