@@ -678,7 +678,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
                     float am[4];
 #pragma unroll
                     for (int m = 0; m < 4; ++m)
-                        am[m] = COLS ? __shfl(alpha, 4 * r + m) : quad_bcast(alpha, m);
+                        am[m] = COLS ? col_bcast(alpha, m) : quad_bcast(alpha, m);
 #pragma unroll
                     for (int e = 0; e < EV; ++e)
 #pragma unroll

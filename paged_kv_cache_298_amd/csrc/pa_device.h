@@ -342,6 +342,39 @@ __device__ __forceinline__ float quad_bcast(float v, int m) {
     return __builtin_bit_cast(float, y);
 }
 
+// Value held by column 4r + m, for a lane of row group r (lanes 16r .. 16r + 15), when all
+// four row groups hold the same per-column values (m a compile-time constant after
+// unrolling). Four DPP row broadcasts (lane n of every 16-lane row to the whole row),
+// each written only to the row group that needs it: no LDS round trip, unlike a lane
+// shuffle.
+#ifndef PA_COL_DPP
+#define PA_COL_DPP 1
+#endif
+template <int M>
+__device__ __forceinline__ int col_bcast_m(int x) {
+    int y = x;
+    y = __builtin_amdgcn_update_dpp(y, x, 0x150 + M, 0x1, 0xf, false);
+    y = __builtin_amdgcn_update_dpp(y, x, 0x150 + 4 + M, 0x2, 0xf, false);
+    y = __builtin_amdgcn_update_dpp(y, x, 0x150 + 8 + M, 0x4, 0xf, false);
+    y = __builtin_amdgcn_update_dpp(y, x, 0x150 + 12 + M, 0x8, 0xf, false);
+    return y;
+}
+__device__ __forceinline__ float col_bcast(float v, int m) {
+#if PA_COL_DPP
+    const int x = __builtin_bit_cast(int, v);
+    int y;
+    switch (m) {
+        case 0: y = col_bcast_m<0>(x); break;
+        case 1: y = col_bcast_m<1>(x); break;
+        case 2: y = col_bcast_m<2>(x); break;
+        default: y = col_bcast_m<3>(x); break;
+    }
+    return __builtin_bit_cast(float, y);
+#else
+    return __shfl(v, 4 * ((int)(threadIdx.x & 63) >> 4) + m);
+#endif
+}
+
 template <int D, int G, int DEPTH, int kChunk, bool QLDS, int W>
 __device__ __forceinline__ void bf16_item(const Params& p, int id) {
     constexpr int ROW = D * 2;              // bytes per cached row

@@ -181,7 +181,7 @@ __device__ __forceinline__ void prefix_item(const Params& p, int id) {
                     // output rows 4r + i of this lane take the factor of column 4r + i
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float ai = __shfl(alpha, 4 * r + i);
+                        const float ai = col_bcast(alpha, i);
 #pragma unroll
                         for (int e = 0; e < EV; ++e) acc[s][e][i] *= ai;
                     }
@@ -485,7 +485,7 @@ __device__ __forceinline__ void multi_item(const Params& p, int id) {
             if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float ai = __shfl(alpha, 4 * r + i);
+                    const float ai = col_bcast(alpha, i);
 #pragma unroll
                     for (int e = 0; e < EV; ++e) acc[s][e][i] *= ai;
                     lsum[s][i] *= ai;
