@@ -293,9 +293,10 @@ int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_
         if (!aligned(workspace, 256))
             return fail(PA_ERR_INVALID_ARG, "pa_decode: workspace must be 256-byte aligned");
     }
-    if (path == pa_internal::kPathPartition && (int64_t)n_parts * Hkv * B > 0x7fffffff)
-        return fail(PA_ERR_UNSUPPORTED, "pa_decode: %lld work items exceed the grid limit",
-                    (long long)n_parts * Hkv * B);
+    if (path == pa_internal::kPathPartition &&
+        ((int64_t)n_parts * Hkv * B > 0x7fffffff || (int64_t)Hq * B > 0x7fffffff))
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: %lld work items (or %lld merged rows) exceed the grid limit",
+                    (long long)n_parts * Hkv * B, (long long)Hq * B);
 
     pa_internal::DecodeLaunch a;
     a.out = out;
@@ -392,7 +393,8 @@ int32_t pa_decode_shared(float* out, const void* q, const void* k_cache, const v
         return fail(PA_ERR_INVALID_ARG, "pa_decode_shared: workspace must be 256-byte aligned");
     // one launch of four items per block: the prefix items, then the suffix partitions
     const int64_t pre_items = (int64_t)n_groups * Hkv * sw.n_pre, suf_items = (int64_t)sw.n_suf * Hkv * B;
-    if (pre_items > 0x7fffffff || suf_items > 0x7fffffff || (pre_items + 3) / 4 + (suf_items + 3) / 4 > 0x7fffffff)
+    if (pre_items > 0x7fffffff || suf_items > 0x7fffffff || (pre_items + 3) / 4 + (suf_items + 3) / 4 > 0x7fffffff ||
+        (int64_t)B * Hq > 0x7fffffff)   // the merge takes one wave per (sequence, query head)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared: work items exceed the grid limit");
 
     pa_internal::SharedLaunch a;

@@ -775,21 +775,21 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
 
 // Merge the partial records of rows that cross slice boundaries. Workgroup w looks at the
 // row holding the first group of slice w; it merges it only when that row began inside
-// slice w - 1, so every split row is merged exactly once. The merge is latency-bound, so
-// the row's records (one per slice it touches, up to ~50 for the longest rows) are dealt
-// to the four waves in contiguous runs: each wave loads its run up to kBatch records at a
-// time, each lane holding F float4 of the row's G x D output, and keeps a running state;
-// the four states are then combined through LDS in wave order. The header and the
-// descriptor are fetched together. The order of every sum is fixed, so results repeat
-// bitwise.
+// slice w - 1, so every split row is merged exactly once. The merge is latency-bound. A
+// narrow row (G x D up to 512 floats) has its records (one per slice it touches, up to
+// ~50 on the longest rows) dealt to the four waves in contiguous runs: each wave loads
+// its run up to kBatch records at a time and keeps a running state, and the four states
+// are combined through LDS in wave order. A wide row (G D / 4 >= 256 float4, records of
+// 4 KiB or more: G = 8 decode, multi-query columns) is split by columns instead, each wave
+// folding every record for its quarter of the row. The header and the descriptor are
+// fetched together. The order of every sum is fixed, so results repeat bitwise.
 template <int D, int G, bool MULTI>
 __global__ __launch_bounds__(256) void stream_reduce_kernel(Params p) {
     constexpr int C4 = D / 4;
     constexpr int NF = G * C4;            // float4s of a row's output
-    constexpr int F = (NF + 63) / 64;     // float4s per lane
+    constexpr bool COLSPLIT = NF >= 256;  // wide rows: each wave takes a quarter of the columns
+    constexpr int F = COLSPLIT ? NF / 256 : (NF + 63) / 64;   // float4s per lane
     constexpr int kBatch = F >= 4 ? 4 : 16 / F;   // records per round trip
-    __shared__ float4 s_o[4][NF];
-    __shared__ float2 s_ml[4][NF];
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
     const int w = blockIdx.x;
@@ -806,14 +806,20 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(Params p) {
     const int wb = (int)(((int64_t)(last + 1) * nwe - 1) / T);   // slice holding the last group
     const int nrec = wb - w + 2;       // slices w - 1 .. wb
     const int rec_a = 2 * (w - 1) + (d.z == s0p ? 0 : 1);
-    // this wave's run of records [xa, xb)
-    const int per = (nrec + 3) >> 2;
-    const int xa = min(nrec, wid * per);
-    const int xb = min(nrec, xa + per);
+    // this wave's run of records [xa, xb) and its float4s of the row
+    int xa = 0, xb = nrec, i0 = 0, istep = 64;
+    if constexpr (COLSPLIT) {
+        i0 = wid * 64 * F;
+    } else {
+        const int per = (nrec + 3) >> 2;
+        xa = min(nrec, wid * per);
+        xb = min(nrec, xa + per);
+        istep = 64;
+    }
     int hh[F], cc[F];                  // head and float4 column of each of the lane's float4s
 #pragma unroll
     for (int f = 0; f < F; ++f) {
-        int i = lane + 64 * f;
+        int i = i0 + lane + istep * f;
         i = i < NF ? i : NF - 1;
         hh[f] = i / C4;
         cc[f] = i - hh[f] * C4;
@@ -868,15 +874,6 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(Params p) {
             M[f] = Mb;
         }
     }
-#pragma unroll
-    for (int f = 0; f < F; ++f) {
-        const int i = lane + 64 * f;
-        if (i < NF) {
-            s_o[wid][i] = o[f];
-            s_ml[wid][i] = make_float2(M[f], l[f]);
-        }
-    }
-    __syncthreads();
     int qs = 0, n = 0;
     if constexpr (MULTI) {
         const int cap = p.max_blocks * p.bs;
@@ -884,22 +881,8 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(Params p) {
         L = L < 0 ? 0 : (L > cap ? cap : L);
         multi_rows(p, d.x, L, &qs, &n);
     }
-    // the four states in wave order; wave 0 holds the row's first record, whose maximum is
-    // finite for every column, so Mx is finite and an empty run weighs 0
-    for (int i = threadIdx.x; i < NF; i += 256) {
-        float2 mlq[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) mlq[q] = s_ml[q][i];
-        const float Mx = fmaxf(fmaxf(mlq[0].x, mlq[1].x), fmaxf(mlq[2].x, mlq[3].x));
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        float lsum = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float wgt = __builtin_amdgcn_exp2f(mlq[q].x - Mx);
-            const float4 oq = s_o[q][i];
-            acc.x += wgt * oq.x; acc.y += wgt * oq.y; acc.z += wgt * oq.z; acc.w += wgt * oq.w;
-            lsum += wgt * mlq[q].y;
-        }
+    // output float4 i (head h = i / C4) of the row
+    auto store = [&](int i, float4 acc, float lsum) {
         const int h = i / C4;
         const int c4 = i - h * C4;
         int64_t orow = (int64_t)d.x * p.Hq + d.y * G + h;
@@ -907,12 +890,46 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(Params p) {
             // column h is query j = h / GK of the row's sequence (none past its query count)
             const int GK = p.Hq / p.Hkv;
             const int j = h / GK;
-            if (j >= n) continue;
+            if (j >= n) return;
             orow = (int64_t)(qs + j) * p.Hq + d.y * GK + (h - j * GK);
         }
         const float inv = 1.0f / lsum;
         reinterpret_cast<float4*>(p.out + orow * D)[c4] =
             make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    };
+    if constexpr (COLSPLIT) {
+#pragma unroll
+        for (int f = 0; f < F; ++f) store(i0 + lane + istep * f, o[f], l[f]);
+    } else {
+        __shared__ float4 s_o[4][NF];
+        __shared__ float2 s_ml[4][NF];
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+            const int i = lane + 64 * f;
+            if (i < NF) {
+                s_o[wid][i] = o[f];
+                s_ml[wid][i] = make_float2(M[f], l[f]);
+            }
+        }
+        __syncthreads();
+        // the four states in wave order; wave 0 holds the row's first record, whose maximum
+        // is finite for every column, so Mx is finite and an empty run weighs 0
+        for (int i = threadIdx.x; i < NF; i += 256) {
+            float2 mlq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) mlq[q] = s_ml[q][i];
+            const float Mx = fmaxf(fmaxf(mlq[0].x, mlq[1].x), fmaxf(mlq[2].x, mlq[3].x));
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            float lsum = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float wgt = __builtin_amdgcn_exp2f(mlq[q].x - Mx);
+                const float4 oq = s_o[q][i];
+                acc.x += wgt * oq.x; acc.y += wgt * oq.y; acc.z += wgt * oq.z; acc.w += wgt * oq.w;
+                lsum += wgt * mlq[q].y;
+            }
+            store(i, acc, lsum);
+        }
     }
 }
 
@@ -929,7 +946,7 @@ hipError_t launch_one(const Params& prm, int B, int Hkv, void* stream) {
                            dim3(prm.n_parts * Hkv * B), dim3(64), lds, s, prm);
     }
     if (prm.n_parts > 1)
-        hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(prm.Hq, B), dim3(256), 0, s, prm);
+        hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3((prm.Hq * B + 3) / 4), dim3(256), 0, s, prm);
     return hipGetLastError();
 }
 

@@ -731,39 +731,42 @@ __device__ __forceinline__ void bf16_item(const Params& p, int id) {
 
 // Combine the partitions of one (sequence, query head):
 // out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i, with M = max_i m_i.
-// Thread (pg, c4) folds partitions pg, pg + NPG, ... of float4 column c4, four per batch,
-// rescaling its running sum when the maximum grows; the NPG partial sums then meet in
-// LDS. The first batch is loaded before the partition count is known, together with the
-// length (and group) that give it: slots below n_parts always lie in the row's workspace,
-// and a slot past the count is dropped by a select, never weighted, since it may hold
-// anything.
+// One wave per row (four rows per workgroup, so a batch of rows takes few workgroups).
+// Lane (pg, c4) folds partitions pg, pg + NPG, ... of float4 column c4, kB per batch,
+// rescaling its running sum when the maximum grows; the NPG partial sums then meet by
+// lane exchanges in a fixed order. The first batch is loaded before the partition count
+// is known, together with the length (and group) that give it: slots below n_parts always
+// lie in the row's workspace, and a slot past the count is dropped by a select, never
+// weighted, since it may hold anything. Rows are (sequence, head), or (query, head) in
+// multi-query mode; the launch covers ceil(rows / 4) workgroups.
 template <int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
-    constexpr int C4 = D / 4;          // float4 columns
-    constexpr int NPG = 256 / C4;      // partition groups per block
-    __shared__ float4 red_o[NPG][C4];
-    __shared__ float2 red_ml[NPG];
-
-    const int h = blockIdx.x;
-    const int y = blockIdx.y;          // the sequence, or in multi-query mode the query
-    const int tid = threadIdx.x;
-    const int c4 = tid % C4;
-    const int pg = tid / C4;
+    constexpr int C4 = D / 4;          // float4 columns (16 or 32)
+    constexpr int NPG = 64 / C4;       // partition groups per wave (4 or 2)
+    constexpr int kB = 8;              // partitions per group per batch
+    const int lane = threadIdx.x & 63;
+    const int c4 = lane % C4;
+    const int pg = lane / C4;
+    const int ny = p.q_starts != nullptr ? p.total_q : p.B;
+    const int rid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    if (rid >= ny * p.Hq) return;
+    const int y = rid / p.Hq;          // the sequence, or in multi-query mode the query
+    const int h = rid - y * p.Hq;
     const int64_t row = (int64_t)y * p.Hq + h;
     const float2* ml = p.ws_ml + row * p.n_parts;
     const float* wo = p.ws_o + row * p.n_parts * D;
-    float2 mlv[4];
-    float4 ov[4];
-    auto load_batch = [&](int i0) {
+    float2 mlv[kB];
+    float4 ov[kB];
+    auto load_batch = [&](int k0) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            int i = i0 + u * NPG;
+        for (int u = 0; u < kB; ++u) {
+            int i = pg + NPG * (k0 + u);
             i = i < p.n_parts ? i : 0;
             mlv[u] = ml[i];
             ov[u] = reinterpret_cast<const float4*>(wo + (int64_t)i * D)[c4];
         }
     };
-    load_batch(pg);
+    load_batch(0);
 
     const int cap = p.max_blocks * p.bs;
     int np;
@@ -793,7 +796,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
             const int start = min(sh, L);
             np = (start + p.pre_tokens - 1) / p.pre_tokens + (L - start + p.part_tokens - 1) / p.part_tokens;
             if (np == 0) {
-                for (int i = tid; i < D; i += 256) p.out[row * D + i] = 0.f;
+                for (int i = lane; i < D; i += 64) p.out[row * D + i] = 0.f;
                 return;
             }
         } else {
@@ -804,18 +807,18 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float den = 0.f, m = -INFINITY;
-    for (int i0 = pg; i0 < np; i0 += 4 * NPG) {
-        if (i0 != pg) load_batch(i0);
+    for (int k0 = 0; pg + NPG * k0 < np; k0 += kB) {
+        if (k0 != 0) load_batch(k0);
         float mn = m;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (i0 + u * NPG < np) mn = fmaxf(mn, mlv[u].x);
+        for (int u = 0; u < kB; ++u)
+            if (pg + NPG * (k0 + u) < np) mn = fmaxf(mn, mlv[u].x);
         const float a = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first batch
         acc.x *= a; acc.y *= a; acc.z *= a; acc.w *= a;
         den *= a;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (i0 + u * NPG < np) {
+        for (int u = 0; u < kB; ++u) {
+            if (pg + NPG * (k0 + u) < np) {
                 const float w = __builtin_amdgcn_exp2f(mlv[u].x - mn);
                 acc.x = fmaf(w, ov[u].x, acc.x);
                 acc.y = fmaf(w, ov[u].y, acc.y);
@@ -826,29 +829,29 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
         }
         m = mn;
     }
-    red_o[pg][c4] = acc;
-    if (c4 == 0) red_ml[pg] = make_float2(m, den);
-    __syncthreads();
+    // the partition groups meet pairwise (lane ^ C4, then lane ^ 2 C4); a group with no
+    // partition holds m = -inf, so a pair of such groups takes 0 as its reference
+#pragma unroll
+    for (int st = C4; st < 64; st <<= 1) {
+        const float om = __shfl_xor(m, st);
+        const float od = __shfl_xor(den, st);
+        const float4 oa = make_float4(__shfl_xor(acc.x, st), __shfl_xor(acc.y, st),
+                                      __shfl_xor(acc.z, st), __shfl_xor(acc.w, st));
+        const float M = fmaxf(m, om);
+        const float Mr = M == -INFINITY ? 0.f : M;
+        const float wa = __builtin_amdgcn_exp2f(m - Mr);
+        const float wb = __builtin_amdgcn_exp2f(om - Mr);
+        acc.x = acc.x * wa + oa.x * wb;
+        acc.y = acc.y * wa + oa.y * wb;
+        acc.z = acc.z * wa + oa.z * wb;
+        acc.w = acc.w * wa + oa.w * wb;
+        den = den * wa + od * wb;
+        m = M;
+    }
     if (pg == 0) {
-        float M = red_ml[0].x;
-#pragma unroll
-        for (int j = 1; j < NPG; ++j) M = fmaxf(M, red_ml[j].x);
-        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-        float dsum = 0.f;
-#pragma unroll
-        for (int j = 0; j < NPG; ++j) {
-            const float2 mlj = red_ml[j];
-            const float w = __builtin_amdgcn_exp2f(mlj.x - M);   // 0 for a group with none
-            const float4 x = red_o[j][c4];
-            sum.x = fmaf(w, x.x, sum.x);
-            sum.y = fmaf(w, x.y, sum.y);
-            sum.z = fmaf(w, x.z, sum.z);
-            sum.w = fmaf(w, x.w, sum.w);
-            dsum = fmaf(w, mlj.y, dsum);
-        }
-        const float inv = 1.0f / dsum;
+        const float inv = 1.0f / den;
         reinterpret_cast<float4*>(p.out + row * D)[c4] =
-            make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
 }
 

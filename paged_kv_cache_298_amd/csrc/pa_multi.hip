@@ -615,7 +615,7 @@ hipError_t launch_shared_d(Params prm, int G, int nset, int n_pre, int n_suf, vo
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(prm.Hq, prm.B), dim3(256), 0, s, prm);
+    hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3((prm.Hq * prm.B + 3) / 4), dim3(256), 0, s, prm);
     return hipGetLastError();
 }
 
@@ -626,7 +626,7 @@ hipError_t launch_multi_d(const Params& prm, int nset, hipStream_t s) {
     else if (nset == 2) hipLaunchKernelGGL((decode_multi_kernel<D, 2>), grid, dim3(256), 0, s, prm);
     else hipLaunchKernelGGL((decode_multi_kernel<D, 4>), grid, dim3(256), 0, s, prm);
     if (prm.n_parts > 1)
-        hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(prm.Hq, prm.total_q), dim3(256), 0, s, prm);
+        hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3((prm.Hq * prm.total_q + 3) / 4), dim3(256), 0, s, prm);
     return hipGetLastError();
 }
 
