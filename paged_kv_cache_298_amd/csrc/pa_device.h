@@ -43,6 +43,11 @@
 #ifndef PA_DECODE_DEPTH
 #define PA_DECODE_DEPTH 4
 #endif
+// Prefill / prompt-chunk tiles: the softmax reference of a query column moves only when
+// its maximum passes it by more than this many log2 units (0: at every new maximum).
+#ifndef PA_LAZY_RESCALE
+#define PA_LAZY_RESCALE 8
+#endif
 
 namespace {
 

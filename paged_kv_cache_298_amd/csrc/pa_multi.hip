@@ -476,13 +476,16 @@ __device__ __forceinline__ void multi_item(const Params& p, int id) {
 #pragma unroll
             for (int i = 1; i < 8; ++i) mx = fmaxf(mx, y[s][i]);
             const float m_new = fmaxf(m_run[s], rows_max(mx));
-            // a column that has seen no token yet keeps m = -inf: use 0 as its reference so
-            // that its factors are exactly 0 instead of NaN
-            const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_ref);   // per column
-            m_run[s] = m_new;
-            // rescale only when some column's maximum moved (a factor of 1 is exact)
-            if (__ballot(alpha != 1.0f) != 0) {
+            // m_run is each column's reference, not always its maximum: it moves (and the
+            // accumulators are rescaled) only when some column's maximum passes its
+            // reference by more than PA_LAZY_RESCALE (log2 units), so the probabilities
+            // stay below 2^PA_LAZY_RESCALE. Softmax does not depend on the reference, and a
+            // column that has seen no token yet moves at its first token. A column with no
+            // token keeps m = -inf and 0 as the exponent reference, so its factors are 0.
+            if (__ballot(m_new > m_run[s] + (float)PA_LAZY_RESCALE) != 0) {
+                const float m_to = m_new == -INFINITY ? 0.f : m_new;
+                const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_to);   // per column
+                m_run[s] = m_new;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float ai = col_bcast(alpha, i);
@@ -491,6 +494,7 @@ __device__ __forceinline__ void multi_item(const Params& p, int id) {
                     lsum[s][i] *= ai;
                 }
             }
+            const float m_ref = m_run[s] == -INFINITY ? 0.f : m_run[s];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const bf16x2_t pp = __builtin_convertvector(
