@@ -167,6 +167,11 @@ STREAM = [
     ("g8-n2", [500, 33, 900], [2, 1, 2], 64, 8, 128, 32),
     ("g2-n3", [129, 400, 3, 64], [3, 3, 3, 1], 16, 8, 128, 16),    # 6 of 8 columns used
     ("g1-n16", [700, 16, 300], [16, 16, 5], 8, 8, 64, 64),
+    # 4 columns (record-split merge); each sequence's last group holds one or two tokens
+    # that the chunk's first query does not see, so with many waves a slice can hold only
+    # segments in which some column sees no token
+    ("g2-n2-edge-d64", [33, 49, 17, 1000, 34], [2, 2, 2, 2, 3], 16, 8, 64, 16),
+    ("g2-n2-edge-d128", [33, 65, 17, 600, 34], [2, 2, 2, 2, 2], 16, 8, 128, 16),
 ]
 
 
