@@ -116,3 +116,82 @@ def test_all_empty_and_fewer_groups_than_waves():
     T, nwe, consumed, produced = _schedule([1, 0, 17], 2, 64, 1)
     assert T == 6 and nwe == 6 and np.all(consumed == 1)
     assert all(v == 1 for v in produced.values())
+
+
+# ------------------------------------------------------------------ the merge's arithmetic
+#
+# The merge kernel folds a split row's records (m_i, l_i, o_i): m_i is the segment's
+# reference in log2 units, l_i its sum and o_i its unnormalised output. Narrow rows deal
+# the records to four waves in contiguous runs, each folded with a running reference in
+# batches, then combine the four states in wave order; wide rows let one wave fold every
+# record. A multi-query column may see no token of a segment (m_i = -inf, l_i = 0,
+# o_i = 0); the row's first record always has a finite reference. This models that
+# arithmetic in float32 and compares it with the plain merge in float64.
+
+def _fold(ms, ls, os_, batch, D):
+    M, l, o = np.float32(-np.inf), np.float32(0), np.zeros(D, dtype=np.float32)
+    for x0 in range(0, len(ms), batch):
+        mb = ms[x0:x0 + batch]
+        Mb = np.float32(max([M] + list(mb)))
+        Mr = np.float32(0) if Mb == -np.inf else Mb       # the kernel's guard
+        a = np.exp2(np.float32(M - Mr))
+        o, l = o * a, l * a
+        for k in range(x0, min(x0 + batch, len(ms))):
+            wgt = np.exp2(np.float32(ms[k] - Mr))
+            o = o + wgt * os_[k]
+            l = l + wgt * ls[k]
+        M = Mb
+    return M, l, o
+
+
+def _merge_four_runs(ms, ls, os_, batch):
+    nrec = len(ms)
+    per = (nrec + 3) // 4
+    runs = [(min(nrec, q * per), min(nrec, min(nrec, q * per) + per)) for q in range(4)]
+    covered = [x for a, b in runs for x in range(a, b)]
+    assert covered == list(range(nrec))                   # contiguous runs, in order
+    st = [_fold(ms[a:b], ls[a:b], os_[a:b], batch, len(os_[0])) for a, b in runs]
+    Mx = np.float32(max(s[0] for s in st))
+    acc = np.zeros_like(os_[0], dtype=np.float32)
+    lsum = np.float32(0)
+    for M, l, o in st:
+        wgt = np.exp2(np.float32(M - Mx))
+        acc, lsum = acc + wgt * o, lsum + wgt * l
+    return acc / lsum
+
+
+def _plain_merge(ms, ls, os_):
+    m = np.array(ms, dtype=np.float64)
+    M = m[np.isfinite(m)].max()
+    w = np.where(np.isfinite(m), np.exp2(np.where(np.isfinite(m), m, 0) - M), 0.0)
+    return (w[:, None] * np.asarray(os_, np.float64)).sum(0) / (w * np.asarray(ls, np.float64)).sum()
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_merge_runs_match_plain_merge(seed):
+    rng = np.random.default_rng(100 + seed)
+    nrec = int(rng.integers(2, 60))
+    D = 8
+    ms = list(rng.normal(0, 6, size=nrec).astype(np.float32))
+    ls = list(rng.uniform(1, 16, size=nrec).astype(np.float32))
+    os_ = [rng.normal(0, 1, size=D).astype(np.float32) * l for l in ls]
+    # a column that sees no token of some later segments (never of the first)
+    for x in rng.choice(np.arange(1, nrec), size=int(rng.integers(0, nrec)), replace=False):
+        ms[x], ls[x], os_[x] = np.float32(-np.inf), np.float32(0), np.zeros(D, np.float32)
+    ref = _plain_merge(ms, ls, os_)
+    for batch in (4, 8, 16):
+        got = _merge_four_runs(ms, ls, os_, batch)             # narrow rows
+        assert np.all(np.isfinite(got)) and np.max(np.abs(got - ref)) < 1e-4
+        M, l, o = _fold(ms, ls, os_, batch, D)                 # wide rows: one fold
+        assert np.max(np.abs(o / l - ref)) < 1e-4
+
+
+def test_merge_guard_is_needed_for_an_all_empty_run():
+    # records 4..7 see no token: with 8 records the fourth wave's run holds only those
+    ms = [np.float32(1.0)] * 4 + [np.float32(-np.inf)] * 4
+    ls = [np.float32(1.0)] * 4 + [np.float32(0.0)] * 4
+    os_ = [np.ones(4, np.float32)] * 4 + [np.zeros(4, np.float32)] * 4
+    assert np.allclose(_merge_four_runs(ms, ls, os_, 8), 1.0)
+    with np.errstate(invalid="ignore"):
+        M = np.float32(-np.inf)
+        assert np.isnan(np.exp2(np.float32(M - M)))           # what the guard avoids
