@@ -496,6 +496,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "decode_us_mean": round(dec_mean, 2),
                      "decode_us_p10": round(float(np.percentile(dec_us, 10)), 2),
+                     "decode_us_p50": round(float(np.median(dec_us)), 2),
                      "decode_us_p90": round(float(np.percentile(dec_us, 90)), 2),
                      "decode_us_hot_one_replica": round(hot_us, 2)},
         "cpu_baseline": cpu,
