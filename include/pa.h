@@ -77,7 +77,9 @@ extern "C" {
  *                 aligned (may be NULL when that size is 0); it holds partial softmax
  *                 states of sequences split across work items and needs no initialisation
  * Supported: D in {64, 128}; block_size in {8, 16, 32, 64, 128} (8 with bf16 caches and
- * the stream decomposition only); G in {1, 2, 4, 8}; others return PA_ERR_UNSUPPORTED. The result is deterministic: repeated calls on one device give
+ * the stream decomposition only); G in {1, 2, 4, 8}; B <= 65535; others, and batches with
+ * more work items or merged rows (B x Hq) than one launch grid holds, return
+ * PA_ERR_UNSUPPORTED. The result is deterministic: repeated calls on one device give
  * identical bits, whatever the physical placement of the blocks.
  *
  * Work decomposition (chosen per call, see pa_set_decode_path):
