@@ -806,20 +806,19 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(Params p) {
     const int wb = (int)(((int64_t)(last + 1) * nwe - 1) / T);   // slice holding the last group
     const int nrec = wb - w + 2;       // slices w - 1 .. wb
     const int rec_a = 2 * (w - 1) + (d.z == s0p ? 0 : 1);
-    // this wave's run of records [xa, xb) and its float4s of the row
-    int xa = 0, xb = nrec, i0 = 0, istep = 64;
+    // this wave's run of records [xa, xb) and its float4s of the row, i0 + lane + 64 f
+    int xa = 0, xb = nrec, i0 = 0;
     if constexpr (COLSPLIT) {
         i0 = wid * 64 * F;
     } else {
         const int per = (nrec + 3) >> 2;
         xa = min(nrec, wid * per);
         xb = min(nrec, xa + per);
-        istep = 64;
     }
     int hh[F], cc[F];                  // head and float4 column of each of the lane's float4s
 #pragma unroll
     for (int f = 0; f < F; ++f) {
-        int i = i0 + lane + istep * f;
+        int i = i0 + lane + 64 * f;
         i = i < NF ? i : NF - 1;
         hh[f] = i / C4;
         cc[f] = i - hh[f] * C4;
@@ -899,7 +898,7 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(Params p) {
     };
     if constexpr (COLSPLIT) {
 #pragma unroll
-        for (int f = 0; f < F; ++f) store(i0 + lane + istep * f, o[f], l[f]);
+        for (int f = 0; f < F; ++f) store(i0 + lane + 64 * f, o[f], l[f]);
     } else {
         __shared__ float4 s_o[4][NF];
         __shared__ float2 s_ml[4][NF];
