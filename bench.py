@@ -465,6 +465,25 @@ def main():
     torch.cuda.synchronize()
     hot_us = float(np.mean([starts[i].elapsed_time(ends[i]) * 1e3 for i in range(n_hot)]))
 
+    # ---- the read ceiling of this access pattern: the same 16-token group tiles, in the
+    # decode kernel's order and slices, read with no arithmetic (pa_read_tiles)
+    read = None
+    if wl.block_size >= 16:
+        elt = 2 if wl.dtype == "bf16" else 4
+        offs = torch.from_numpy(W.group_tile_offsets(wl.block_tables, wl.seq_lens, wl.Hkv, wl.D,
+                                                     elt, wl.block_size)).to(dev)
+        sink = torch.zeros(pa.READ_SINK_LEN, dtype=torch.int32, device=dev)
+        tile = 16 * wl.D * elt
+        rd = _per_call_us(torch, lambda r: pa.pa_read_tiles(r["k"], r["v"], offs, tile, sink,
+                                                           stream=stream),
+                          reps, args.steps, args.warmup, stream)
+        read = {"kernel": "pa_read_tiles: the decode kernel's tiles, order and slices, no arithmetic",
+                "us_mean": rd["mean"], "us_p50": rd["p50"],
+                "GBps": round(kv_bytes / (rd["mean"] * 1e-6) / 1e9, 2),
+                "decode_frac_of_read": round(rd["mean"] / dec_mean, 4)}
+        _log(f"read ceiling: mean {rd['mean']:.1f} us ({read['GBps']:.0f} GB/s of KV); "
+             f"pa_decode at {read['decode_frac_of_read']:.3f} of it")
+
     achieved = kv_bytes / (dec_mean * 1e-6) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     cpu = None
@@ -498,7 +517,7 @@ def main():
                      "decode_us_p10": round(float(np.percentile(dec_us, 10)), 2),
                      "decode_us_p50": round(float(np.median(dec_us)), 2),
                      "decode_us_p90": round(float(np.percentile(dec_us, 90)), 2),
-                     "decode_us_hot_one_replica": round(hot_us, 2)},
+                     "decode_us_hot_one_replica": round(hot_us, 2), "read_ceiling": read},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -238,6 +238,32 @@ int32_t pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
                        int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
                        int32_t kv_dtype, void* stream);
 
+/* ------------------------------------------------------------------ read-ceiling aid */
+
+/*
+ * pa_read_tiles -- a measurement aid, not part of the attention path: the HBM read rate
+ * the decode kernel could reach on its own access pattern. It reads n_tiles tiles of
+ * tile_bytes from K and the same bytes from V, tile i at byte offset tile_offsets[i] of
+ * both caches, in the order given, the way the stream decode kernel reads its 16-token
+ * groups (one wavefront per SIMD, equal contiguous slices of the list, non-temporal
+ * 16-byte loads), and does no arithmetic but an XOR of every loaded 32-bit word into one
+ * value per wavefront.
+ *
+ *   k_cache, v_cache  device, 16-byte aligned, cache_bytes each
+ *   tile_offsets      device int64 [n_tiles]; each a multiple of 16 with
+ *                     offset + tile_bytes <= cache_bytes (not checked on the device)
+ *   tile_bytes        1024, 2048, 4096, 8192 or 16384 (a 16-token group of one KV head:
+ *                     16 x D x element bytes)
+ *   sink              device uint32 [4096]; entry w receives the XOR of the words read by
+ *                     wavefront w (entries past the device's resident wavefronts are left
+ *                     as they are), so the XOR of all entries is the XOR of every word of
+ *                     the listed tiles of both caches
+ * n_tiles == 0 launches nothing. Asynchronous on `stream`.
+ */
+int32_t pa_read_tiles(const void* k_cache, const void* v_cache, size_t cache_bytes,
+                      const int64_t* tile_offsets, int32_t n_tiles, int32_t tile_bytes,
+                      uint32_t* sink, void* stream);
+
 /* ------------------------------------------------------------------ status */
 
 const char* pa_status_string(int32_t status);

@@ -591,6 +591,28 @@ int32_t pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
     return ok();
 }
 
+int32_t pa_read_tiles(const void* k_cache, const void* v_cache, size_t cache_bytes,
+                      const int64_t* tile_offsets, int32_t n_tiles, int32_t tile_bytes,
+                      uint32_t* sink, void* stream) {
+    if (n_tiles < 0 || (tile_bytes != 1024 && tile_bytes != 2048 && tile_bytes != 4096 &&
+                        tile_bytes != 8192 && tile_bytes != 16384))
+        return fail(PA_ERR_INVALID_ARG, "pa_read_tiles: bad sizes n_tiles=%d tile_bytes=%d (1024..16384, a power of 2)",
+                    n_tiles, tile_bytes);
+    if (n_tiles == 0) return ok();
+    if (!k_cache || !v_cache || !tile_offsets || !sink)
+        return fail(PA_ERR_INVALID_ARG, "pa_read_tiles: null pointer argument");
+    if (cache_bytes < (size_t)tile_bytes)
+        return fail(PA_ERR_INVALID_ARG, "pa_read_tiles: caches of %zu bytes hold no tile of %d bytes",
+                    cache_bytes, tile_bytes);
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(tile_offsets, 8) || !aligned(sink, 4))
+        return fail(PA_ERR_INVALID_ARG, "pa_read_tiles: misaligned pointer");
+    const char* err = "";
+    const int e = pa_internal::launch_read_tiles(k_cache, v_cache, tile_offsets, n_tiles, tile_bytes,
+                                                 sink, stream, &err);
+    if (e != 0) return fail(PA_ERR_HIP, "pa_read_tiles: launch failed: %s (%d)", err, e);
+    return ok();
+}
+
 }  // extern "C"
 
 namespace pa_internal {

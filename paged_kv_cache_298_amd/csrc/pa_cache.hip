@@ -10,6 +10,8 @@
 //   (subroutine-cs.cc), section 3.
 // Both are bit copies moved in 16-byte units, one unit per lane per access, consecutive
 // lanes on consecutive units, so every wave-wide access is 1 KiB of contiguous bytes.
+// read_tiles (pa_read_tiles): a measurement aid, not part of the attention path; it reads
+//   a list of K/V tiles the way the stream decode kernel does, with no arithmetic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -76,6 +78,60 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4_t* __restrict__ 
     }
 }
 
+// Read-ceiling aid (pa_read_tiles): stream a given list of tiles, each tile_bytes of K at
+// a byte offset and the same bytes of V at that offset, the way the stream decode kernel
+// reads its 16-token groups -- one wave per SIMD, equal contiguous slices of the list,
+// the offsets of 64 tiles at a time held in lanes, non-temporal 16-byte loads -- but with
+// no arithmetic: every loaded word is folded by XOR into one value per wave, which keeps
+// the loads live and lets the result be checked bit for bit. NCH = tile_bytes / 1024;
+// about 32 loads per lane are in flight per batch.
+template <int NCH>
+__global__ __launch_bounds__(256) void read_tiles_kernel(const char* __restrict__ k,
+                                                         const char* __restrict__ v,
+                                                         const int64_t* __restrict__ offs, int n,
+                                                         int nw, uint32_t* __restrict__ sink) {
+    constexpr int TB = NCH >= 16 ? 1 : 16 / NCH;   // tiles per batch
+    const int lane = threadIdx.x & 63;
+    const int w = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (w >= nw) return;
+    const int s0 = (int)((int64_t)w * n / nw);
+    const int s1 = (int)((int64_t)(w + 1) * n / nw);
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+    for (int base = s0; base < s1; base += 64) {
+        int idx = base + lane;
+        idx = idx < s1 ? idx : s1 - 1;
+        const int64_t my = offs[idx];
+        const uint32_t my_lo = (uint32_t)my, my_hi = (uint32_t)((uint64_t)my >> 32);
+        const int cnt = min(64, s1 - base);
+        for (int u0 = 0; u0 < cnt; u0 += TB) {
+            u32x4_t r[TB][2 * NCH];
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                const int tt = min(u0 + t, cnt - 1);
+                const int64_t off = (int64_t)(((uint64_t)__builtin_amdgcn_readlane(my_hi, tt) << 32) |
+                                              (uint64_t)__builtin_amdgcn_readlane(my_lo, tt));
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) {
+                    r[t][i] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4_t*>(k + off + i * 1024 + lane * 16));
+                    r[t][NCH + i] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4_t*>(v + off + i * 1024 + lane * 16));
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+                if (u0 + t < cnt) {
+#pragma unroll
+                    for (int i = 0; i < 2 * NCH; ++i) acc ^= r[t][i];
+                }
+        }
+    }
+    uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) x ^= (uint32_t)__shfl_xor((int)x, d);
+    if (lane == 0) sink[w] = x;
+}
+
 }  // namespace
 
 namespace pa_internal {
@@ -116,6 +172,40 @@ int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
                            units, (int)num_blocks);
     }
     const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        *err = hipGetErrorString(e);
+        return (int)e;
+    }
+    return 0;
+}
+
+int launch_read_tiles(const void* k, const void* v, const int64_t* offs, int32_t n,
+                      int32_t tile_bytes, uint32_t* sink, void* stream, const char** err) {
+    // one 4-wave workgroup per CU, as the stream decode kernel runs: each workgroup
+    // reserves just over half of a CU's LDS, so no CU takes two
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    int dev = 0, cus = 0, per_cu = 0, per_block = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e == hipSuccess) {
+        int nw = cus * 4;
+        nw = nw > kMaxStreamWaves ? kMaxStreamWaves : nw;
+        size_t lds = (size_t)per_cu / 2 + 1024;
+        if (lds > (size_t)per_block) lds = 0;
+        const dim3 grid((nw + 3) / 4), block(256);
+        const char* kc = static_cast<const char*>(k);
+        const char* vc = static_cast<const char*>(v);
+        switch (tile_bytes) {
+            case 1024: hipLaunchKernelGGL(read_tiles_kernel<1>, grid, block, lds, st, kc, vc, offs, n, nw, sink); break;
+            case 2048: hipLaunchKernelGGL(read_tiles_kernel<2>, grid, block, lds, st, kc, vc, offs, n, nw, sink); break;
+            case 4096: hipLaunchKernelGGL(read_tiles_kernel<4>, grid, block, lds, st, kc, vc, offs, n, nw, sink); break;
+            case 8192: hipLaunchKernelGGL(read_tiles_kernel<8>, grid, block, lds, st, kc, vc, offs, n, nw, sink); break;
+            default: hipLaunchKernelGGL(read_tiles_kernel<16>, grid, block, lds, st, kc, vc, offs, n, nw, sink); break;
+        }
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) {
         *err = hipGetErrorString(e);
         return (int)e;

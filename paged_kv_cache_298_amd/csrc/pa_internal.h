@@ -122,6 +122,8 @@ int launch_reshape_and_cache(void* k_cache, void* v_cache, const void* key, cons
                              void* stream, const char** err);
 int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t N,
                        int64_t block_bytes, int32_t num_blocks, void* stream, const char** err);
+int launch_read_tiles(const void* k, const void* v, const int64_t* offs, int32_t n,
+                      int32_t tile_bytes, uint32_t* sink, void* stream, const char** err);
 
 // Thread-local error message of the C ABI (pa_last_error); set_error returns status.
 int32_t set_error(int32_t status, const char* msg);

@@ -41,6 +41,7 @@ _SIGS = {
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                     _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_read_tiles": (_i32, [_vp, _vp, _sz, _vp, _i32, _i32, _vp, _vp]),
     "pa_status_string": (ctypes.c_char_p, [_i32]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_abi_version": (_i32, []),
@@ -216,6 +217,22 @@ def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None):
     N = block_pairs.shape[0]
     _check(_lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs), N, Hkv, D, bs, nb,
                                _kv_dtype(k_cache), _stream(k_cache, stream)))
+
+
+READ_SINK_LEN = 4096   # uint32 entries pa_read_tiles' sink must hold
+
+
+def pa_read_tiles(k_cache, v_cache, tile_offsets, tile_bytes, sink, stream=None):
+    """Read-ceiling aid: stream the listed tiles of both caches (int64 byte offsets, in
+    order) as the stream decode kernel reads its groups, XOR-folding every word into
+    sink (uint32 [READ_SINK_LEN]); no attention arithmetic."""
+    if sink.dtype != torch.int32 or sink.numel() < READ_SINK_LEN:
+        raise ValueError(f"sink must be an int32 tensor of at least {READ_SINK_LEN} entries")
+    if tile_offsets.dtype != torch.int64:
+        raise TypeError("tile_offsets must be int64")
+    _check(_lib.pa_read_tiles(_ptr(k_cache), _ptr(v_cache), k_cache.numel() * k_cache.element_size(),
+                              _ptr(tile_offsets), tile_offsets.numel(), int(tile_bytes), _ptr(sink),
+                              _stream(k_cache, stream)))
 
 
 class BlockAllocator:

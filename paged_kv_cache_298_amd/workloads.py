@@ -346,3 +346,24 @@ def config(n, poison=True, keep_logical=False):
 def kv_bytes_per_token(layers, kv_heads, head_dim, elt_bytes):
     """Bytes of K plus V per token: 2 (K and V) x elt_bytes x layers x kv_heads x head_dim."""
     return 2 * elt_bytes * layers * kv_heads * head_dim
+
+
+def group_tile_offsets(block_tables, seq_lens, Hkv, D, elt_bytes, block_size):
+    """Byte offsets (int64, into either cache) of every 16-token group tile that the stream
+    decode kernel reads, in its order: sequences, then KV heads, then groups. A tile is
+    16 rows of D elements of one KV head inside one block (block_size >= 16)."""
+    assert block_size >= 16 and block_size % 16 == 0
+    row = D * elt_bytes
+    tile = block_size * row                 # one (block, KV head) tile
+    blk = Hkv * tile                        # one physical block
+    out = []
+    for b, L in enumerate(np.asarray(seq_lens)):
+        n = (int(L) + 15) // 16
+        if n == 0:
+            continue
+        j = np.arange(n, dtype=np.int64)
+        phys = np.asarray(block_tables[b], dtype=np.int64)[(j * 16) // block_size]
+        base = phys * blk + ((j * 16) % block_size) * row
+        for g in range(Hkv):
+            out.append(base + g * tile)
+    return np.concatenate(out) if out else np.zeros(0, dtype=np.int64)

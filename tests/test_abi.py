@@ -266,3 +266,21 @@ def test_decode_multi_workspace_and_empty_batch():
     # too many columns for the stream decomposition
     assert pa.pa_decode_multi_workspace_bytes(4, 4096, 1024, 32, 8, 128, 16, 256) == 0
     assert pa.pa_decode_multi_workspace_bytes(0, 4, 4, 32, 8, 128, 16, 256) == 0
+
+
+def test_read_tiles_validation():
+    lib = pa._lib
+    call = lambda **kw: lib.pa_read_tiles(
+        kw.get("k", FAKE), kw.get("v", FAKE), kw.get("cache_bytes", 1 << 20), kw.get("offs", FAKE),
+        kw.get("n", 4), kw.get("tile_bytes", 4096), kw.get("sink", FAKE), None)
+    assert call(n=0) == pa.PA_OK                                  # nothing to read: no launch
+    assert call(n=0, k=None, v=None, offs=None, sink=None) == pa.PA_OK
+    for bad in (0, 512, 3072, 32768, -4096):
+        assert call(tile_bytes=bad) == pa.PA_ERR_INVALID_ARG
+    assert call(n=-1) == pa.PA_ERR_INVALID_ARG
+    for name in ("k", "v", "offs", "sink"):
+        assert call(**{name: None}) == pa.PA_ERR_INVALID_ARG
+    assert call(cache_bytes=2048) == pa.PA_ERR_INVALID_ARG       # no whole tile fits
+    assert call(k=ctypes.c_void_p(0x100008)) == pa.PA_ERR_INVALID_ARG
+    assert call(offs=ctypes.c_void_p(0x100004)) == pa.PA_ERR_INVALID_ARG
+    assert "pa_read_tiles" in lib.pa_last_error().decode()

@@ -15,7 +15,7 @@ import torch
 
 from paged_kv_cache_298_amd import workloads as W
 from tests._gpu_helpers import (DEV, TOL, DevWorkload, gpu_step, max_err, note, oracle_step,
-                                to_host)
+                                to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -475,3 +475,31 @@ def test_one_token_returns_its_value_exactly(pa):
             v = W.bf16_to_f32(v) if dt == W.BF16 else v
             for h in range(8):
                 assert np.array_equal(out[b, h], v[h // 4])
+
+
+# ------------------------------------------------------------------ read-ceiling aid
+
+@pytest.mark.parametrize("D,dtype", [(128, W.BF16), (64, W.BF16), (128, W.F32)],
+                         ids=["d128-bf16", "d64-bf16", "d128-f32"])
+def test_read_tiles_xor_matches_host(pa, D, dtype):
+    """pa_read_tiles reads exactly the listed tiles of both caches: the XOR of its sink
+    equals the XOR of every 32-bit word of those tiles, computed on the host."""
+    rng = np.random.default_rng(D)
+    L = rng.integers(1, 700, size=24).astype(np.int32)
+    wl = W.make_workload(f"read-{D}", 24, 32, 8, D, 16, L, dtype, seed=D, poison=True)
+    elt = 2 if dtype == W.BF16 else 4
+    offs = W.group_tile_offsets(wl.block_tables, wl.seq_lens, wl.Hkv, wl.D, elt, 16)
+    tile = 16 * D * elt
+    kr = np.ascontiguousarray(wl.k_cache).view(np.uint8).reshape(-1)
+    vr = np.ascontiguousarray(wl.v_cache).view(np.uint8).reshape(-1)
+    assert offs.min() >= 0 and offs.max() + tile <= kr.size   # host guard before the launch
+    note(f"read_tiles D={D} {dtype} tiles={len(offs)} tile_bytes={tile}")
+    k, v = to_dev(wl.k_cache), to_dev(wl.v_cache)
+    sink = torch.zeros(pa.READ_SINK_LEN, dtype=torch.int32, device=DEV)
+    pa.pa_read_tiles(k, v, torch.from_numpy(offs).to(DEV), tile, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    idx = (offs[:, None] + np.arange(tile)[None, :]).reshape(-1)
+    want = (np.bitwise_xor.reduce(kr[idx].view(np.uint32)) ^
+            np.bitwise_xor.reduce(vr[idx].view(np.uint32)))
+    assert got == want
