@@ -31,7 +31,7 @@ class PrefixCacheRef:
 
     def _evictable(self, exclude=()):
         return [e for e, (blk, _, _) in self.info.items()
-                if self.mgr.ref(blk) == 1 and e not in exclude]
+                if self.mgr.holders_of(blk) == 1 and e not in exclude]
 
     def _evict(self, n, exclude=()):
         done = 0
@@ -40,7 +40,7 @@ class PrefixCacheRef:
                 break
             blk, _, key = self.info.pop(e)
             del self.entries[key]
-            self.mgr.free_blocks([blk])
+            self.mgr.give_back([blk])
             done += 1
         return done
 
@@ -56,13 +56,13 @@ class PrefixCacheRef:
             hits.append(e)
             parent = e
         need = total - len(hits)
-        spare = len(self.mgr.free)
+        spare = len(self.mgr.stack)
         if spare < need and spare + len(self._evictable(exclude=set(hits))) < need:
             raise OutOfBlocks(f"out of KV blocks: need {need}")
-        table = self.mgr.fork([self.info[e][0] for e in hits])
+        table = self.mgr.share([self.info[e][0] for e in hits])
         if spare < need:
             self._evict(need - spare, exclude=set(hits))
-        table += self.mgr.allocate(need)
+        table += self.mgr.take(need)
         for e in hits:
             self._touch(e)
         return table, len(hits) * bs
@@ -71,7 +71,7 @@ class PrefixCacheRef:
         bs = self.bs
         tokens = [int(t) for t in tokens]
         full = len(tokens) // bs
-        if full > len(table) or any(self.mgr.ref(b) < 1 for b in table[:full]):
+        if full > len(table) or any(self.mgr.holders_of(b) < 1 for b in table[:full]):
             raise ValueError("publish: table does not hold the tokens")
         parent = 0
         for i in range(full):
@@ -80,7 +80,7 @@ class PrefixCacheRef:
             if e is None:
                 e = self.next_id
                 self.next_id += 1
-                self.mgr.fork([table[i]])
+                self.mgr.share([table[i]])
                 self.entries[key] = e
                 self.info[e] = [table[i], 0, key]
             self._touch(e)

@@ -139,14 +139,14 @@ def test_cow_through_the_append_path(pa, oracle):
     """A prompt that ends inside a block (2040 tokens, bs 16) forked 4 ways; each fork
     appends one token through the reference block manager: three clone the shared last
     block (copy old -> new), the last writes in place."""
-    from oracle.block_manager import BlockManager, Sequence
+    from oracle.block_manager import Pool, SeqTable
     bs, prompt, nf = 16, 2040, 4
     base = W.make_workload("cow", 1, 32, 8, 128, bs, [prompt], W.BF16, seed=77, max_blocks=160,
                            num_blocks=200, keep_logical=True)
-    mgr = BlockManager(base.num_blocks, bs,
-                       initial_free=[int(x) for x in np.random.default_rng(1).permutation(base.num_blocks)])
-    root = Sequence(mgr, prompt)
-    seqs = [root] + [root.fork() for _ in range(nf - 1)]
+    mgr = Pool(base.num_blocks, bs,
+               free_order=[int(x) for x in np.random.default_rng(1).permutation(base.num_blocks)])
+    root = SeqTable(mgr, prompt)
+    seqs = [root] + [root.branch() for _ in range(nf - 1)]
     rng = np.random.default_rng(2)
     k = np.full_like(base.k_cache, W.NAN_BF16)
     v = np.full_like(base.v_cache, W.NAN_BF16)
@@ -155,7 +155,7 @@ def test_cow_through_the_append_path(pa, oracle):
         v[root.table[t // bs], :, t % bs] = base.logical_v[0][t]
     pairs, slots = [], []
     for s in seqs:
-        slot, cow = s.append_token()
+        slot, cow = s.add_token()
         slots.append(slot)
         if cow:
             pairs.append(cow)
