@@ -75,7 +75,8 @@ extern "C" {
  *   scale         softmax scale, applied in fp32 to the fp32 dot product
  *   workspace     device scratch of at least pa_decode_workspace_bytes(...) bytes, 256-byte
  *                 aligned (may be NULL when that size is 0); it holds partial softmax
- *                 states of sequences split across work items and needs no initialisation
+ *                 states of sequences split across work items and needs no
+ *                 initialisation. Calls that share one workspace must not overlap.
  * Supported: D in {64, 128}; block_size in {8, 16, 32, 64, 128} (8 with bf16 caches and
  * the stream decomposition only); G in {1, 2, 4, 8}; B <= 65535; others, and batches with
  * more work items or merged rows (B x Hq) than one launch grid holds, return
@@ -86,7 +87,8 @@ extern "C" {
  *   stream     (bf16 caches, B <= 4096, fewer than 2^31 groups of 16 tokens in the batch):
  *              the batch's (sequence, KV head) rows, cut into 16-token groups, are laid
  *              end to end and every resident wavefront of the device takes an equal
- *              contiguous slice; rows that cross slices are merged by a second kernel.
+ *              contiguous slice; rows that cross slices are merged, in a fixed order, by
+ *              a second kernel.
  *   partition  (otherwise): one work item per (sequence, KV head, partition of
  *              pa_decode_partition_tokens tokens), then a merge of the partitions.
  */
@@ -97,9 +99,20 @@ int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_
                   size_t workspace_bytes, void* stream);
 
 /*
- * Workspace bytes pa_decode needs for these sizes and element type, whichever
- * decomposition it picks (0 when none needs any): an upper bound taken from the
- * host-known max_blocks. Returns 0 for sizes pa_decode would reject.
+ * Workspace bytes pa_decode needs for these sizes and element type with the decomposition
+ * it picks under the current pa_set_decode_path setting (0 when it needs none); an upper
+ * bound from the host-known max_blocks. Returns 0 for sizes pa_decode would reject. A
+ * change of the path, partition or wave settings changes the size: query it again.
+ *   Hkv and kv_dtype are needed because the decomposition depends on them: bf16 caches
+ *   take the stream decomposition, whose partial records hold the G = Hq / Hkv query
+ *   heads of a KV head, two per wavefront that gets a slice: 2 x ns x G x (D + 2) x 4
+ *   bytes plus 16 bytes per launched wavefront nw. nw is the number of wavefronts the
+ *   current device holds at once (4096 when no device is visible); ns <= nw is no more
+ *   than the batch fills with 8 groups of 16 tokens each (pa_set_stream_waves changes
+ *   both).
+ *   fp32 caches take the partition decomposition: B x Hq x n_parts x (D + 2) x 4 bytes when
+ *   a sequence can span more than one partition of pa_decode_partition_tokens tokens, else 0.
+ * The size depends on the current device; allocate it on the device the calls run on.
  */
 size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
                                  int32_t max_blocks, int32_t kv_dtype);

@@ -77,19 +77,36 @@ bool stream_eligible(int32_t kv_dtype, int32_t B, int32_t Hkv, int32_t block_siz
     return (int64_t)B * Hkv * groups < ((int64_t)1 << 31);
 }
 
+// Stream decomposition workspace, each section 256-byte aligned: two partial records per
+// wave that gets a slice (outputs [G, D] and (max, sum) pairs [G]), one descriptor per
+// launched wave and a 4-int header. G counts the query columns of a row (heads, or heads x
+// query tokens in the multi-query mode).
 struct StreamWs {
     size_t ml, desc, meta, total;
 };
 
-StreamWs stream_workspace(int32_t G, int32_t D) {
-    const size_t W2 = 2 * (size_t)pa_internal::kMaxStreamWaves;
+StreamWs stream_workspace(int32_t G, int32_t D, int32_t slices, int32_t launched) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t W2 = 2 * (size_t)slices;
     StreamWs w;
     w.ml = up(W2 * (size_t)G * (size_t)D * sizeof(float));
     w.desc = up(w.ml + W2 * (size_t)G * 2 * sizeof(float));
-    w.meta = up(w.desc + (size_t)pa_internal::kMaxStreamWaves * 4 * sizeof(int32_t));
+    w.meta = up(w.desc + (size_t)launched * 4 * sizeof(int32_t));
     w.total = w.meta + 4 * sizeof(int32_t);
     return w;
+}
+
+// Waves a stream launch starts (the device's resident waves; kMaxStreamWaves when no
+// device can be queried) and, of those, the most that get a slice: no more than the batch
+// fills with min_slice groups each (T <= B Hkv ceil(capacity / 16) groups).
+StreamWs stream_workspace_for(int32_t B, int32_t Hkv, int32_t G, int32_t D, int32_t block_size,
+                              int32_t max_blocks) {
+    int32_t nw = 0;
+    if (pa_internal::stream_waves(g_stream_waves, &nw) != 0 || nw <= 0) nw = pa_internal::kMaxStreamWaves;
+    const int64_t gmax = ((int64_t)block_size * max_blocks + 15) / 16;
+    int64_t fill = (int64_t)B * Hkv * gmax / (g_min_slice > 0 ? g_min_slice : 1);
+    fill = fill < 1 ? 1 : fill;
+    return stream_workspace(G, D, fill < nw ? (int32_t)fill : nw, nw);
 }
 
 // Blocks of 8 tokens (a 16-token group spans two blocks) are served by the stream
@@ -151,7 +168,7 @@ MultiWs multi_workspace(int32_t B, int32_t total_q, int32_t max_q, int32_t Hq, i
         w.total = w.ml + rows * 2 * sizeof(float);
     }
     w.stream_g = multi_stream_g(B, max_q, Hq, Hkv, block_size, max_blocks);
-    w.sws = stream_workspace(w.stream_g > 0 ? w.stream_g : 4, D);
+    w.sws = stream_workspace_for(B, Hkv, w.stream_g > 0 ? w.stream_g : 4, D, block_size, max_blocks);
     // enough for either decomposition, so the size does not depend on the path setting
     if (w.stream_g > 0 && w.sws.total > w.total) w.total = w.sws.total;
     return w;
@@ -231,11 +248,13 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, 
                                  int32_t max_blocks, int32_t kv_dtype) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || block_size <= 0 || max_blocks <= 0)
         return 0;
+    // the decomposition pa_decode picks for these sizes under the current path setting
+    const int32_t path = choose_path(kv_dtype, B, Hkv, block_size, max_blocks);
+    if (path == pa_internal::kPathStream)
+        return stream_workspace_for(B, Hkv, Hq / Hkv, D, block_size, max_blocks).total;
+    if (path != pa_internal::kPathPartition) return 0;
     size_t ml;
-    const size_t part = workspace_layout(B, Hq, D, n_parts_for(block_size, max_blocks), &ml);
-    const size_t strm = stream_eligible(kv_dtype, B, Hkv, block_size, max_blocks)
-                            ? stream_workspace(Hq / Hkv, D).total : 0;
-    return part > strm ? part : strm;
+    return workspace_layout(B, Hq, D, n_parts_for(block_size, max_blocks), &ml);
 }
 
 int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
@@ -283,7 +302,7 @@ int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_
         return fail(PA_ERR_INVALID_ARG, "pa_decode: partition %d not a multiple of block_size %d", P, block_size);
     const int32_t n_parts = n_parts_for(block_size, max_blocks);
     size_t ml_off = 0;
-    const StreamWs sws = stream_workspace(G, D);
+    const StreamWs sws = stream_workspace_for(B, Hkv, G, D, block_size, max_blocks);
     const size_t need = path == pa_internal::kPathStream ? sws.total
                                                          : workspace_layout(B, Hq, D, n_parts, &ml_off);
     if (need > 0) {

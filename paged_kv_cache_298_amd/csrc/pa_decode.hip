@@ -994,11 +994,10 @@ template <int D, int G, bool SPLIT, bool MULTI = false, bool DIST = false>
 hipError_t launch_stream(Params prm, int nw_req, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     size_t lds = (size_t)(2 * prm.B + 1) * sizeof(int);
-    int nw = nw_req;
-    if (nw <= 0) {
-        const int e = stream_shape(lds, &nw, &lds);
-        if (e != 0) return (hipError_t)e;
-    }
+    int nw = 0;
+    const int e = stream_shape(lds, &nw, &lds);
+    if (e != 0) return (hipError_t)e;
+    if (nw_req > 0) nw = nw_req;
     nw = nw > pa_internal::kMaxStreamWaves ? pa_internal::kMaxStreamWaves : nw;
     nw = (nw + 3) / 4 * 4;
     prm.nw = nw;
@@ -1039,6 +1038,17 @@ hipError_t dispatch_d(const Params& prm, int B, int Hkv, int D, int G, void* str
 }  // namespace
 
 namespace pa_internal {
+
+int stream_waves(int32_t override_waves, int32_t* nw) {
+    int n = 0;
+    size_t lds = 0;
+    const int e = stream_shape(0, &n, &lds);
+    if (e != 0) return e;
+    if (override_waves > 0) n = override_waves;
+    n = n > kMaxStreamWaves ? kMaxStreamWaves : n;
+    *nw = (n + 3) / 4 * 4;
+    return 0;
+}
 
 int launch_decode(const DecodeLaunch& a, const char** err) {
     Params prm{};   // zero: no shared-prefix groups, no stream records

@@ -25,9 +25,9 @@ struct DecodeLaunch {
     void* stream;
     // stream decomposition (path == kPathStream)
     int32_t path;            // kPathPartition or kPathStream
-    float* rec_o;            // [2 * kMaxStreamWaves, G, D]
-    float* rec_ml;           // [2 * kMaxStreamWaves, G, 2]
-    int32_t* desc;           // [kMaxStreamWaves, 4]
+    float* rec_o;            // [2 * slices, G, D]
+    float* rec_ml;           // [2 * slices, G, 2]
+    int32_t* desc;           // [launched waves, 4]
     int32_t* meta;           // [4]
     int32_t stream_waves;    // 0 = every wave the device holds at once
     int32_t min_slice;       // fewest 16-token groups per wave
@@ -110,6 +110,11 @@ MultiPlan multi_plan(int32_t B, int32_t max_q, int32_t Hq, int32_t Hkv, int32_t 
 #endif
 constexpr int kMultiMinWaves = PA_MULTI_MIN_WAVES;   // split the tokens until this many items exist
 constexpr int kMultiMinPart = PA_MULTI_MIN_PART;     // ... but not below this many tokens per partition
+
+// Waves the stream decomposition launches on the current device: override_waves (> 0,
+// rounded up to a multiple of 4), else one per SIMD; at most kMaxStreamWaves. Returns 0, or
+// a HIP error code when the device cannot be queried.
+int stream_waves(int32_t override_waves, int32_t* nw);
 
 // Each returns 0 on success or a nonzero HIP error code (message in *err).
 int launch_decode(const DecodeLaunch& a, const char** err);

@@ -134,8 +134,8 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, workspace
               stream=None):
     """out [B, Hq, D] fp32 <- paged decode attention. k_cache/v_cache are
     [num_blocks, Hkv, block_size, D]; block_tables int32 [B, max_blocks]; seq_lens int32 [B].
-    workspace: a uint8 tensor of at least pa_decode_workspace_bytes(...) bytes, zero-filled
-    before its first use (allocated here, zeroed, on q's device, when None and needed)."""
+    workspace: a uint8 tensor of at least pa_decode_workspace_bytes(...) bytes (allocated
+    here on q's device when None and needed)."""
     B, Hq, D = q.shape
     nb, Hkv, bs, _ = k_cache.shape
     max_blocks = block_tables.shape[1]
@@ -192,7 +192,7 @@ def pa_decode_multi(out, q, k_cache, v_cache, block_tables, seq_lens, q_starts, 
     max_blocks = block_tables.shape[1]
     need = pa_decode_multi_workspace_bytes(B, total_q, max_q, Hq, Hkv, D, bs, max_blocks)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.pa_decode_multi(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                 _ptr(block_tables), _ptr(seq_lens), _ptr(q_starts), B, total_q,

@@ -93,11 +93,15 @@ def _up(x):
     return (x + 255) // 256 * 256
 
 
-def _stream_ws(G, D, waves=4096):
-    """Record layout of the stream decomposition: partial outputs, (max, sum) pairs, one
-    descriptor per wave, then a 4-int header; each section 256-byte aligned."""
-    ml = _up(2 * waves * G * D * 4)
-    desc = _up(ml + 2 * waves * G * 8)
+def _stream_ws(G, D, B, Hkv, capacity, waves=4096, min_slice=8):
+    """Layout of the stream decomposition's workspace: partial outputs and (max, sum) pairs
+    for two records per wave that gets a slice, one descriptor per launched wave, then a
+    4-int header; each section 256-byte aligned. Launched waves: the device's (4096 with no
+    device visible); waves with a slice: no more than the batch fills with min_slice groups
+    of 16 tokens."""
+    slices = max(1, min(waves, B * Hkv * (-(-capacity // 16)) // min_slice))
+    ml = _up(2 * slices * G * D * 4)
+    desc = _up(ml + 2 * slices * G * 8)
     meta = _up(desc + waves * 16)
     return meta + 16
 
@@ -117,9 +121,15 @@ def test_workspace_bytes_and_partitions():
     o = rows * 128 * 4
     part = _up(o) + rows * 8
     assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 256, F32) == part
-    # bf16 caches: room for whichever decomposition is chosen
-    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 256, BF16) == max(part, _stream_ws(4, 128))
-    assert pa.pa_decode_workspace_bytes(4, 2, 1, 64, 16, 3, BF16) == _stream_ws(2, 64)
+    # bf16 caches: the stream decomposition's records (the default path), or the partitions'
+    # when that path is forced
+    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 256, BF16) == _stream_ws(4, 128, 64, 8, 4096)
+    pa.pa_set_decode_path(pa.PA_PATH_PARTITION)
+    try:
+        assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 256, BF16) == part
+    finally:
+        pa.pa_set_decode_path(pa.PA_PATH_AUTO)
+    assert pa.pa_decode_workspace_bytes(4, 2, 1, 64, 16, 3, BF16) == _stream_ws(2, 64, 4, 1, 48)
     # past the stream limits (B > 4096) bf16 falls back to partitions
     assert pa.pa_decode_workspace_bytes(5000, 8, 8, 64, 16, 3, BF16) == 0
     assert pa.pa_decode_workspace_bytes(4, 6, 4, 64, 16, 3, BF16) == 0      # Hq % Hkv != 0
@@ -260,7 +270,7 @@ def test_decode_multi_workspace_and_empty_batch():
     # stream decomposition (4 x 4 = 16 query columns) needs records for 2 x 4096 slices
     rows = 256 * 32 * 4
     tiles = _up(rows * 128 * 4) + rows * 8
-    stream = _up(_up(_up(8192 * 16 * 128 * 4) + 8192 * 16 * 8) + 4096 * 16) + 16
+    stream = _stream_ws(16, 128, 64, 8, 4096)
     assert pa.pa_decode_multi_workspace_bytes(64, 256, 4, 32, 8, 128, 16, 256) == max(tiles, stream)
     # 1024-token chunks of 4 sequences: 64 tiles each, enough items without a split, and
     # too many columns for the stream decomposition
