@@ -251,6 +251,61 @@ int32_t pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
                        int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
                        int32_t kv_dtype, void* stream);
 
+/* ------------------------------------------------------------------ debug validation */
+
+/*
+ * The kernels read device-resident indices without checking them against the
+ * preconditions stated above (they clamp what they read, so a violation never reaches
+ * outside the buffers, but the rows it touches come out wrong and nothing reports it).
+ * The debug validation pass checks them: a table entry for each of a sequence's
+ * ceil(L / block_size) logical blocks ([P1] "Interpret Block Tables"; [P2] section 4
+ * "Tiny example", PhysicalIndex), one slot per new token, and copy-on-write clones into
+ * fresh blocks that are then written ([P2] section 5 "Copy-on-write sharing": copy first,
+ * then write), i.e. distinct destinations none of which another pair copies from.
+ *
+ * Flags of a validation (bitwise OR of every kind found):
+ */
+#define PA_BAD_LENGTH 0x1         /* seq_lens[b] outside [0, max_blocks * block_size] */
+#define PA_BAD_TABLE_ENTRY 0x2    /* block_tables[b][j], j < ceil(L_b / block_size), outside [0, num_blocks) */
+#define PA_BAD_SLOT 0x4           /* slot_mapping[i] >= num_blocks * block_size */
+#define PA_DUP_SLOT 0x8           /* two tokens name the same non-negative slot */
+#define PA_BAD_PAIR 0x10          /* a block_pairs index outside [0, num_blocks) */
+#define PA_DUP_DST 0x20           /* two pairs copy into the same block */
+#define PA_DST_IS_SRC 0x40        /* a destination block is also some pair's source */
+#define PA_BAD_GROUP 0x80         /* pa_decode_shared groups break their preconditions */
+#define PA_BAD_QUERY_STARTS 0x100 /* pa_decode_multi q_starts break their preconditions */
+
+/*
+ * Debug mode, process-wide (default off; PA_VALIDATE=1 in the environment when the
+ * library first checks turns it on): every kernel entry point first copies its index
+ * arrays (tables, lengths, slots, pairs, groups, query offsets) to the host on its own
+ * stream, waits for them, and checks them; on a violation it returns PA_ERR_INVALID_ARG,
+ * pa_last_error() names the first one, and nothing is enqueued. The calls then block the
+ * host: for debugging, not for timing. pa_set_validation(on) takes 0 or 1.
+ */
+int32_t pa_set_validation(int32_t on);
+int32_t pa_validation_enabled(void);
+
+/*
+ * Host validators (host pointers; the same checks the debug mode runs). Each returns
+ * PA_OK, or PA_ERR_INVALID_ARG with pa_last_error() naming the first violation; *flags
+ * (nullable) receives the PA_BAD_* / PA_DUP_* flags of all of them. Shapes as for the
+ * kernel entry points; groups as for pa_decode_shared, q_starts as for pa_decode_multi.
+ */
+int32_t pa_validate_decode(const int32_t* block_tables, const int32_t* seq_lens, int32_t B,
+                           int32_t block_size, int32_t num_blocks, int32_t max_blocks,
+                           uint32_t* flags);
+int32_t pa_validate_slots(const int32_t* slot_mapping, int32_t T, int32_t block_size,
+                          int32_t num_blocks, uint32_t* flags);
+int32_t pa_validate_block_pairs(const int32_t* block_pairs, int32_t N, int32_t num_blocks,
+                                uint32_t* flags);
+int32_t pa_validate_groups(const int32_t* groups, int32_t n_groups, const int32_t* block_tables,
+                           const int32_t* seq_lens, int32_t B, int32_t block_size,
+                           int32_t max_blocks, int32_t max_members, int32_t max_shared_tokens,
+                           uint32_t* flags);
+int32_t pa_validate_query_starts(const int32_t* q_starts, const int32_t* seq_lens, int32_t B,
+                                 int32_t total_q, int32_t max_q, uint32_t* flags);
+
 /* ------------------------------------------------------------------ read-ceiling aid */
 
 /*
@@ -264,7 +319,9 @@ int32_t pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
  *
  *   k_cache, v_cache  device, 16-byte aligned, cache_bytes each
  *   tile_offsets      device int64 [n_tiles]; each a multiple of 16 with
- *                     offset + tile_bytes <= cache_bytes (not checked on the device)
+ *                     offset + tile_bytes <= cache_bytes; the kernel clamps an offset
+ *                     outside [0, cache_bytes - tile_bytes] into it and rounds it down to
+ *                     16 bytes, so no load leaves the caches
  *   tile_bytes        1024, 2048, 4096, 8192 or 16384 (a 16-token group of one KV head:
  *                     16 x D x element bytes)
  *   sink              device uint32 [4096]; entry w receives the XOR of the words read by

@@ -11,7 +11,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# PA_ORACLE_LIBRARY: another build of the same source (the sanitizer check uses it)
+_LIB_PATH = os.environ.get("PA_ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 F32, BF16 = 0, 1

@@ -317,6 +317,12 @@ int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_
         return fail(PA_ERR_UNSUPPORTED, "pa_decode: %lld work items (or %lld merged rows) exceed the grid limit",
                     (long long)n_parts * Hkv * B, (long long)Hq * B);
 
+    if (pa_internal::validation_on()) {
+        const int32_t st = pa_internal::validate_decode_device("pa_decode", block_tables, seq_lens, B, block_size,
+                                                               num_blocks, max_blocks, stream);
+        if (st != PA_OK) return st;
+    }
+
     pa_internal::DecodeLaunch a;
     a.out = out;
     char* ws = static_cast<char*>(workspace);
@@ -416,6 +422,13 @@ int32_t pa_decode_shared(float* out, const void* q, const void* k_cache, const v
         (int64_t)B * Hq > 0x7fffffff)   // the merge takes one wave per (sequence, query head)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared: work items exceed the grid limit");
 
+    if (pa_internal::validation_on()) {
+        const int32_t st = pa_internal::validate_shared_device(block_tables, seq_lens, groups, n_groups, B,
+                                                               block_size, num_blocks, max_blocks,
+                                                               max_members, max_shared_tokens, stream);
+        if (st != PA_OK) return st;
+    }
+
     pa_internal::SharedLaunch a;
     a.out = out;
     a.ws_o = static_cast<float*>(workspace);
@@ -512,6 +525,12 @@ int32_t pa_decode_multi(float* out, const void* q, const void* k_cache, const vo
             return fail(PA_ERR_INVALID_ARG, "pa_decode_multi: workspace must be 256-byte aligned");
     }
 
+    if (pa_internal::validation_on()) {
+        const int32_t st = pa_internal::validate_multi_device(block_tables, seq_lens, q_starts, B, total_q, max_q,
+                                                              block_size, num_blocks, max_blocks, stream);
+        if (st != PA_OK) return st;
+    }
+
     pa_internal::MultiLaunch a;
     a.out = out;
     a.ws_o = mw.total > 0 ? static_cast<float*>(workspace) : nullptr;
@@ -577,6 +596,10 @@ int32_t pa_reshape_and_cache(void* k_cache, void* v_cache, const void* key, cons
     if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(key, 16) || !aligned(value, 16) ||
         !aligned(slot_mapping, 4))
         return fail(PA_ERR_INVALID_ARG, "pa_reshape_and_cache: misaligned pointer");
+    if (pa_internal::validation_on()) {
+        const int32_t st = pa_internal::validate_slots_device(slot_mapping, T, block_size, num_blocks, stream);
+        if (st != PA_OK) return st;
+    }
     const char* err = "";
     const int e = pa_internal::launch_reshape_and_cache(k_cache, v_cache, key, value, slot_mapping,
                                                         T, Hkv, D * eb, block_size, num_blocks,
@@ -603,6 +626,10 @@ int32_t pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
         return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: null pointer argument");
     if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_pairs, 4))
         return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: misaligned pointer");
+    if (pa_internal::validation_on()) {
+        const int32_t st = pa_internal::validate_pairs_device(block_pairs, N, num_blocks, stream);
+        if (st != PA_OK) return st;
+    }
     const char* err = "";
     const int e = pa_internal::launch_copy_blocks(k_cache, v_cache, block_pairs, N, block_bytes,
                                                   num_blocks, stream, &err);
@@ -626,7 +653,7 @@ int32_t pa_read_tiles(const void* k_cache, const void* v_cache, size_t cache_byt
     if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(tile_offsets, 8) || !aligned(sink, 4))
         return fail(PA_ERR_INVALID_ARG, "pa_read_tiles: misaligned pointer");
     const char* err = "";
-    const int e = pa_internal::launch_read_tiles(k_cache, v_cache, tile_offsets, n_tiles, tile_bytes,
+    const int e = pa_internal::launch_read_tiles(k_cache, v_cache, cache_bytes, tile_offsets, n_tiles, tile_bytes,
                                                  sink, stream, &err);
     if (e != 0) return fail(PA_ERR_HIP, "pa_read_tiles: launch failed: %s (%d)", err, e);
     return ok();

@@ -85,11 +85,14 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4_t* __restrict__ 
 // no arithmetic: every loaded word is folded by XOR into one value per wave, which keeps
 // the loads live and lets the result be checked bit for bit. NCH = tile_bytes / 1024;
 // about 32 loads per lane are in flight per batch.
+// Offsets are clamped into [0, max_off] and rounded down to 16 bytes (max_off =
+// cache_bytes - tile_bytes, itself a multiple of 16), so every load stays inside the caches.
 template <int NCH>
 __global__ __launch_bounds__(256) void read_tiles_kernel(const char* __restrict__ k,
                                                          const char* __restrict__ v,
                                                          const int64_t* __restrict__ offs, int n,
-                                                         int nw, uint32_t* __restrict__ sink) {
+                                                         int nw, int64_t max_off,
+                                                         uint32_t* __restrict__ sink) {
     constexpr int TB = NCH >= 16 ? 1 : 16 / NCH;   // tiles per batch
     const int lane = threadIdx.x & 63;
     const int w = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
@@ -100,7 +103,9 @@ __global__ __launch_bounds__(256) void read_tiles_kernel(const char* __restrict_
     for (int base = s0; base < s1; base += 64) {
         int idx = base + lane;
         idx = idx < s1 ? idx : s1 - 1;
-        const int64_t my = offs[idx];
+        int64_t my = offs[idx];
+        my = my < 0 ? 0 : (my > max_off ? max_off : my);
+        my &= ~(int64_t)15;
         const uint32_t my_lo = (uint32_t)my, my_hi = (uint32_t)((uint64_t)my >> 32);
         const int cnt = min(64, s1 - base);
         for (int u0 = 0; u0 < cnt; u0 += TB) {
@@ -179,7 +184,18 @@ int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
     return 0;
 }
 
-int launch_read_tiles(const void* k, const void* v, const int64_t* offs, int32_t n,
+int copy_to_host(void* dst, const void* src, size_t bytes, void* stream, const char** err) {
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+        *err = hipGetErrorString(e);
+        return (int)e;
+    }
+    return 0;
+}
+
+int launch_read_tiles(const void* k, const void* v, size_t cache_bytes, const int64_t* offs, int32_t n,
                       int32_t tile_bytes, uint32_t* sink, void* stream, const char** err) {
     // one 4-wave workgroup per CU, as the stream decode kernel runs: each workgroup
     // reserves just over half of a CU's LDS, so no CU takes two
@@ -197,12 +213,13 @@ int launch_read_tiles(const void* k, const void* v, const int64_t* offs, int32_t
         const dim3 grid((nw + 3) / 4), block(256);
         const char* kc = static_cast<const char*>(k);
         const char* vc = static_cast<const char*>(v);
+        const int64_t mo = (int64_t)((cache_bytes - (size_t)tile_bytes) & ~(size_t)15);
         switch (tile_bytes) {
-            case 1024: hipLaunchKernelGGL(read_tiles_kernel<1>, grid, block, lds, st, kc, vc, offs, n, nw, sink); break;
-            case 2048: hipLaunchKernelGGL(read_tiles_kernel<2>, grid, block, lds, st, kc, vc, offs, n, nw, sink); break;
-            case 4096: hipLaunchKernelGGL(read_tiles_kernel<4>, grid, block, lds, st, kc, vc, offs, n, nw, sink); break;
-            case 8192: hipLaunchKernelGGL(read_tiles_kernel<8>, grid, block, lds, st, kc, vc, offs, n, nw, sink); break;
-            default: hipLaunchKernelGGL(read_tiles_kernel<16>, grid, block, lds, st, kc, vc, offs, n, nw, sink); break;
+            case 1024: hipLaunchKernelGGL(read_tiles_kernel<1>, grid, block, lds, st, kc, vc, offs, n, nw, mo, sink); break;
+            case 2048: hipLaunchKernelGGL(read_tiles_kernel<2>, grid, block, lds, st, kc, vc, offs, n, nw, mo, sink); break;
+            case 4096: hipLaunchKernelGGL(read_tiles_kernel<4>, grid, block, lds, st, kc, vc, offs, n, nw, mo, sink); break;
+            case 8192: hipLaunchKernelGGL(read_tiles_kernel<8>, grid, block, lds, st, kc, vc, offs, n, nw, mo, sink); break;
+            default: hipLaunchKernelGGL(read_tiles_kernel<16>, grid, block, lds, st, kc, vc, offs, n, nw, mo, sink); break;
         }
         e = hipGetLastError();
     }

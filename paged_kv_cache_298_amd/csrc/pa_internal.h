@@ -127,8 +127,28 @@ int launch_reshape_and_cache(void* k_cache, void* v_cache, const void* key, cons
                              void* stream, const char** err);
 int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t N,
                        int64_t block_bytes, int32_t num_blocks, void* stream, const char** err);
-int launch_read_tiles(const void* k, const void* v, const int64_t* offs, int32_t n,
+int launch_read_tiles(const void* k, const void* v, size_t cache_bytes, const int64_t* offs, int32_t n,
                       int32_t tile_bytes, uint32_t* sink, void* stream, const char** err);
+
+// Debug validation pass (validate.cpp): whether it is on, and the checks each kernel entry
+// point runs on host copies of its device index arrays (PA_OK or a status with the message
+// set).
+bool validation_on();
+int32_t validate_decode_device(const char* who, const int32_t* tables, const int32_t* lens, int32_t B,
+                               int32_t block_size, int32_t num_blocks, int32_t max_blocks, void* stream);
+int32_t validate_shared_device(const int32_t* tables, const int32_t* lens, const int32_t* groups,
+                               int32_t n_groups, int32_t B, int32_t block_size, int32_t num_blocks,
+                               int32_t max_blocks, int32_t max_members, int32_t max_shared_tokens,
+                               void* stream);
+int32_t validate_multi_device(const int32_t* tables, const int32_t* lens, const int32_t* q_starts,
+                              int32_t B, int32_t total_q, int32_t max_q, int32_t block_size,
+                              int32_t num_blocks, int32_t max_blocks, void* stream);
+int32_t validate_slots_device(const int32_t* slots, int32_t T, int32_t block_size, int32_t num_blocks,
+                              void* stream);
+int32_t validate_pairs_device(const int32_t* pairs, int32_t N, int32_t num_blocks, void* stream);
+// bytes from device memory to host memory on `stream`, waiting for the copy (0 or a HIP
+// error code, message in *err)
+int copy_to_host(void* dst, const void* src, size_t bytes, void* stream, const char** err);
 
 // Thread-local error message of the C ABI (pa_last_error); set_error returns status.
 int32_t set_error(int32_t status, const char* msg);

@@ -11,7 +11,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpa.so")
+# PA_LIBRARY: another build of the same sources (the sanitizer check uses it)
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpa.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} not found: build it with __graft_entry__.build() "
                       "(or python paged_kv_cache_298_amd/build.py)")
@@ -42,6 +43,13 @@ _SIGS = {
                                     _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_read_tiles": (_i32, [_vp, _vp, _sz, _vp, _i32, _i32, _vp, _vp]),
+    "pa_set_validation": (_i32, [_i32]),
+    "pa_validation_enabled": (_i32, []),
+    "pa_validate_decode": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "pa_validate_slots": (_i32, [_vp, _i32, _i32, _i32, _vp]),
+    "pa_validate_block_pairs": (_i32, [_vp, _i32, _i32, _vp]),
+    "pa_validate_groups": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_validate_query_starts": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
     "pa_status_string": (ctypes.c_char_p, [_i32]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_abi_version": (_i32, []),
@@ -68,6 +76,11 @@ for _name, (_res, _args) in _SIGS.items():
     _fn.argtypes = _args
 
 EXPORTS = tuple(_SIGS)
+
+
+# flags of the debug validation pass (include/pa.h)
+PA_BAD_LENGTH, PA_BAD_TABLE_ENTRY, PA_BAD_SLOT, PA_DUP_SLOT = 0x1, 0x2, 0x4, 0x8
+PA_BAD_PAIR, PA_DUP_DST, PA_DST_IS_SRC, PA_BAD_GROUP, PA_BAD_QUERY_STARTS = 0x10, 0x20, 0x40, 0x80, 0x100
 
 
 class PaError(RuntimeError):
@@ -351,3 +364,60 @@ class PrefixCache:
 
     def num_entries(self):
         return int(_lib.pa_pcache_num_entries(self._h))
+
+
+# ---------------------------------------------------------------- debug validation
+
+def pa_set_validation(on):
+    """Debug mode: every kernel entry point checks its index arrays on the host first and
+    raises PaError (PA_ERR_INVALID_ARG) on a violation, with nothing enqueued."""
+    _check(_lib.pa_set_validation(1 if on else 0))
+
+
+def pa_validation_enabled():
+    return bool(_lib.pa_validation_enabled())
+
+
+def _host_i32(a):
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _validate(fn, *args):
+    """(status, flags, message) of a host validator; status PA_OK or PA_ERR_INVALID_ARG."""
+    flags = ctypes.c_uint32(0)
+    st = fn(*args, ctypes.byref(flags))
+    return st, int(flags.value), (_lib.pa_last_error().decode() if st != PA_OK else "")
+
+
+def pa_validate_decode(block_tables, seq_lens, block_size, num_blocks):
+    t, tp = _host_i32(block_tables)
+    l, lp = _host_i32(seq_lens)
+    return _validate(_lib.pa_validate_decode, tp, lp, int(t.shape[0]), int(block_size),
+                     int(num_blocks), int(t.shape[1]))
+
+
+def pa_validate_slots(slot_mapping, block_size, num_blocks):
+    s, sp = _host_i32(slot_mapping)
+    return _validate(_lib.pa_validate_slots, sp, int(s.shape[0]), int(block_size), int(num_blocks))
+
+
+def pa_validate_block_pairs(block_pairs, num_blocks):
+    p, pp = _host_i32(block_pairs)
+    return _validate(_lib.pa_validate_block_pairs, pp, int(p.reshape(-1, 2).shape[0]), int(num_blocks))
+
+
+def pa_validate_groups(groups, block_tables, seq_lens, block_size, max_members, max_shared_tokens):
+    g, gp = _host_i32(groups)
+    t, tp = _host_i32(block_tables)
+    l, lp = _host_i32(seq_lens)
+    return _validate(_lib.pa_validate_groups, gp, int(g.reshape(-1, 3).shape[0]), tp, lp,
+                     int(t.shape[0]), int(block_size), int(t.shape[1]), int(max_members),
+                     int(max_shared_tokens))
+
+
+def pa_validate_query_starts(q_starts, seq_lens, max_q):
+    q, qp = _host_i32(q_starts)
+    l, lp = _host_i32(seq_lens)
+    return _validate(_lib.pa_validate_query_starts, qp, lp, int(l.shape[0]), int(q[-1]), int(max_q))
