@@ -68,25 +68,50 @@ def _traffic_for(config_name):
     return entry.get("bytes_per_launch") if entry else None
 
 
-def _cpu_baseline(wl, budget_s):
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _cpu_baseline(wl, budget_s, one_thread=False):
+    """The fp64 oracle on the whole step (copy_blocks if any, cache write, decode of every
+    row), repeated for about budget_s on all the host threads OpenMP offers; with
+    one_thread, also on one thread for about half as long (at least one step)."""
     from oracle import oracle as orc
     threads = orc.max_threads()
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        kc, vc = wl.k_cache, wl.v_cache
-        if wl.cow_pairs.shape[0]:
-            kc, vc = orc.copy_blocks(kc, vc, wl.cow_pairs)
-        kc, vc = orc.reshape_and_cache(kc, vc, wl.new_key, wl.new_value, wl.slot_mapping)
-        orc.decode(wl.q, kc, vc, wl.block_tables, wl.seq_lens, wl.scale)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 200:
-            break
-    per = el / reps
-    return {"value": round(wl.kv_bytes() / per / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "seconds_per_step": round(per, 4),
-            "sample": f"the full step (cache write + fp64 decode of all {wl.B} sequences) "
-                      f"repeated {reps}x, {el:.1f} s"}
+
+    def run(n_threads, budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            kc, vc = wl.k_cache, wl.v_cache
+            if wl.cow_pairs.shape[0]:
+                kc, vc = orc.copy_blocks(kc, vc, wl.cow_pairs)
+            kc, vc = orc.reshape_and_cache(kc, vc, wl.new_key, wl.new_value, wl.slot_mapping)
+            orc.decode(wl.q, kc, vc, wl.block_tables, wl.seq_lens, wl.scale, threads=n_threads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget or reps >= 200:
+                return el / reps, reps, el
+
+    per, reps, el = run(threads, budget_s)
+    out = {"value": round(wl.kv_bytes() / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+           "kind": "oracle", "seconds_per_step": round(per, 4), "cpu_model": _cpu_model(),
+           "sample": f"the full step (cache write + fp64 decode of all {wl.B} sequences) "
+                     f"repeated {reps}x, {el:.1f} s"}
+    if one_thread:
+        per1, reps1, el1 = run(1, budget_s / 2)
+        out["one_thread"] = {"value": round(wl.kv_bytes() / per1 / 1e9, 4), "unit": "GB/s",
+                             "seconds_per_step": round(per1, 4),
+                             "sample": f"the same step on 1 thread, repeated {reps1}x, {el1:.1f} s"}
+        orc.decode(wl.q[:1], wl.k_cache, wl.v_cache, wl.block_tables[:1], wl.seq_lens[:1], wl.scale,
+                   threads=threads)   # OpenMP keeps the last thread count: restore it
+    return out
 
 
 def _cpu_timed(run, budget_s):
@@ -116,6 +141,23 @@ def _copy_calibration(torch, pa, dev, launches=5):
     per = 2 * npairs * 8 * 16 * 128 * 2
     print(json.dumps({"calibration": "pa_copy_blocks", "launches": launches,
                       "bytes_read_per_launch": per, "bytes_written_per_launch": per}), flush=True)
+
+
+def _read_calibration(torch, pa, W, dev, launches=5):
+    """pa_read_tiles over the Llama-3-8B batch's tile list: non-temporal 16-byte loads, as
+    the decode kernel issues them, of a known number of bytes (every K and V tile of the
+    batch once), the reference for scaling rocprofv3 FETCH_SIZE of the decode kernel."""
+    wl = W.config(2, poison=False)
+    k, v = _to_dev(wl.k_cache, torch, dev), _to_dev(wl.v_cache, torch, dev)
+    offs = torch.from_numpy(W.group_tile_offsets(wl.block_tables, wl.seq_lens, wl.Hkv, wl.D, 2,
+                                                 wl.block_size)).to(dev)
+    sink = torch.zeros(pa.READ_SINK_LEN, dtype=torch.int32, device=dev)
+    for _ in range(launches):
+        pa.pa_read_tiles(k, v, offs, 16 * wl.D * 2, sink)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "pa_read_tiles (non-temporal)", "launches": launches,
+                      "bytes_read_per_launch": int(offs.numel()) * 16 * wl.D * 2 * 2,
+                      "bytes_written_per_launch": 4 * pa.READ_SINK_LEN}), flush=True)
 
 
 def _sweep_block_size(torch, pa, W, dev, args):
@@ -359,6 +401,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run pa_copy_blocks over a known number of bytes (the reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and print them")
+    ap.add_argument("--read-calibration", action="store_true",
+                    help="only run pa_read_tiles (non-temporal loads) over the Llama-3-8B "
+                         "batch's tiles, a known number of bytes, and print them")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="the shared-prefix batch through pa_decode_shared and pa_decode; "
                          "one JSON line")
@@ -380,6 +425,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         _copy_calibration(torch, pa, dev)
+        return
+    if args.read_calibration:
+        _read_calibration(torch, pa, W, dev)
         return
     if args.sweep_block_size:
         _sweep_block_size(torch, pa, W, dev, args)
@@ -437,13 +485,15 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
     _log(f"step: {ms_step * 1e3:.1f} us (events), {wall_ms * 1e3:.1f} us (wall)")
 
-    # ---- pa_decode alone: events around every call, on its stream
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for i in range(args.warmup):
+    # ---- pa_decode alone: events around every call, on its stream; at least 200 calls
+    # after at least 30 warm-up calls, so the mean and percentiles are stable
+    n_dec, w_dec = max(args.steps, 200), max(args.warmup, 30)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_dec)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_dec)]
+    for i in range(w_dec):
         decode_only(reps[i % R])
     torch.cuda.synchronize()
-    for i in range(args.steps):
+    for i in range(n_dec):
         starts[i].record(stream)
         decode_only(reps[i % R])
         ends[i].record(stream)
@@ -457,7 +507,7 @@ def main():
     for i in range(args.warmup):
         decode_only(reps[0])
     torch.cuda.synchronize()
-    n_hot = min(args.steps, 50)
+    n_hot = 50
     for i in range(n_hot):
         starts[i].record(stream)
         decode_only(reps[0])
@@ -476,7 +526,7 @@ def main():
         tile = 16 * wl.D * elt
         rd = _per_call_us(torch, lambda r: pa.pa_read_tiles(r["k"], r["v"], offs, tile, sink,
                                                            stream=stream),
-                          reps, args.steps, args.warmup, stream)
+                          reps, n_dec, w_dec, stream)
         read = {"kernel": "pa_read_tiles: the decode kernel's tiles, order and slices, no arithmetic",
                 "us_mean": rd["mean"], "us_p50": rd["p50"],
                 "GBps": round(kv_bytes / (rd["mean"] * 1e-6) / 1e9, 2),
@@ -489,7 +539,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         _log("cpu baseline (oracle)")
-        cpu = _cpu_baseline(wl, args.cpu_seconds)
+        cpu = _cpu_baseline(wl, args.cpu_seconds, one_thread=args.config in (1, 2))
 
     traffic = _traffic_for(wl.name)
     line = {
@@ -517,7 +567,8 @@ def main():
                      "decode_us_p10": round(float(np.percentile(dec_us, 10)), 2),
                      "decode_us_p50": round(float(np.median(dec_us)), 2),
                      "decode_us_p90": round(float(np.percentile(dec_us, 90)), 2),
-                     "decode_us_hot_one_replica": round(hot_us, 2), "read_ceiling": read},
+                     "decode_us_hot_one_replica": round(hot_us, 2), "decode_calls_timed": n_dec,
+                     "read_ceiling": read},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

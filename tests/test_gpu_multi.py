@@ -2,8 +2,8 @@
 tokens) with the oracle, on an MI355X, through the C ABI.
 
 Each step writes the chunk's K/V with pa_reshape_and_cache, then runs pa_decode_multi.
-Max-abs error over every output element <= 2e-2 (bf16 caches, fp32 accumulation); at
-full size the oracle computes a seeded sample of rows.
+Max-abs error over every output element <= 2e-2 (bf16 caches, fp32 accumulation), at
+full size too.
 """
 import numpy as np
 import pytest
@@ -130,16 +130,24 @@ def test_placement_leaves_multi_bitwise_equal(pa):
     assert np.array_equal(outs[0], outs[1])
 
 
-def test_draft_tokens_llama3_batch_sampled(pa, oracle):
-    """The Llama-3-8B batch's lengths with four draft tokens per sequence, at full size;
-    the oracle computes 256 seeded rows."""
+def test_draft_tokens_llama3_batch_full(pa, oracle):
+    """The Llama-3-8B batch's lengths with four draft tokens per sequence, at full size,
+    every one of its 256 x 32 query rows against the oracle (the multi-query bench batch)."""
     rng = np.random.default_rng(29802)
     lens = rng.integers(1, 4097, size=64).astype(np.int32)
     lens = np.maximum(lens, 4)
     wl = W.make_workload("mq-llama3-draft", 64, 32, 8, 128, 16, lens, W.BF16, seed=29802,
                          max_blocks=256, n_new=[4] * 64)
-    rows = np.sort(np.random.default_rng(7).choice(int(wl.q_starts[-1]) * 32, 256, replace=False)).astype(np.int32)
-    _parity(pa, oracle, wl, "llama3 draft", rows=rows)
+    _parity(pa, oracle, wl, "llama3 draft")
+
+
+def test_prompt_chunks_bench_batch_full(pa, oracle):
+    """The chunked-prefill bench batch: 1024-token chunks of 4 sequences after 0, 1024, 2048
+    and 3072 cached tokens (64 query tiles per row, lazy rescale over up to 4096 tokens),
+    every output row against the oracle."""
+    wl = W.make_workload("chunks", 4, 32, 8, 128, 16, [1024, 2048, 3072, 4096], W.BF16, 29806,
+                         max_blocks=256, n_new=[1024] * 4)
+    _parity(pa, oracle, wl, "chunk bench batch")
 
 
 def test_loose_max_q_bound_and_empty_chunks(pa, oracle):

@@ -213,6 +213,77 @@ def test_cow_through_the_append_path(pa, oracle):
 
 # ------------------------------------------------------------------ bit-exact kernels
 
+def test_steps_built_by_the_product_allocator(pa, oracle):
+    """Every table, slot and copy-on-write pair comes from the product allocator
+    (pa_alloc_allocate / fork / append_token): four prompts (2040, 2048, 333 and 17 tokens,
+    the first ending inside a block) are written by pa_reshape_and_cache, forked 16, 8, 4
+    and 2 ways, then every sequence appends three tokens, one per round, each round being
+    pa_copy_blocks (the clones its appends asked for) -> pa_reshape_and_cache; then
+    pa_decode. Caches must equal the oracle's replay of the same calls bit for bit, and the
+    output must match the oracle's attention."""
+    from tests._gpu_helpers import to_dev
+    bs, Hq, Hkv, D, max_blocks, nb = 16, 32, 8, 128, 160, 640
+    rng = np.random.default_rng(2040)
+    alloc = pa.BlockAllocator(nb, bs, initial_free_order=rng.permutation(nb).astype(np.int32))
+    k = np.full((nb, Hkv, bs, D), W.NAN_BF16, np.uint16)
+    v = np.full_like(k, W.NAN_BF16)
+    kd, vd = to_dev(k), to_dev(v)
+    kc, vc = k, v
+
+    def rand_rows(n):
+        return W.bf16_from_f32(rng.standard_normal((n, Hkv, D), dtype=np.float32))
+
+    def write(nk, nv, slots):
+        nonlocal kc, vc
+        st = pa.pa_validate_slots(slots, bs, nb)
+        assert st[0] == pa.PA_OK, st
+        pa.pa_reshape_and_cache(kd, vd, to_dev(nk), to_dev(nv), to_dev(np.asarray(slots, np.int32)))
+        kc, vc = oracle.reshape_and_cache(kc, vc, nk, nv, np.asarray(slots, np.int32))
+
+    tables, lens = [], []
+    for L, forks in ((2040, 16), (2048, 8), (333, 4), (17, 2)):
+        t = alloc.allocate(-(-L // bs))
+        note(f"allocator-driven: prompt of {L} tokens in blocks {t[:4]}..., {forks} forks")
+        write(rand_rows(L), rand_rows(L), [t[p // bs] * bs + p % bs for p in range(L)])
+        tables += [t] + [alloc.fork(t) for _ in range(forks - 1)]
+        lens += [L] * forks
+    n_pairs = 0
+    for rnd in range(3):
+        slots, pairs = [], []
+        for i in range(len(tables)):
+            lens[i], slot, cow = alloc.append_token(tables[i], lens[i], table_cap=max_blocks)
+            slots.append(slot)
+            if cow:
+                pairs.append(cow)
+        note(f"allocator-driven round {rnd}: {len(pairs)} clone pairs")
+        if pairs:
+            pairs = np.asarray(pairs, np.int32)
+            st = pa.pa_validate_block_pairs(pairs, nb)
+            assert st[0] == pa.PA_OK, st
+            pa.pa_copy_blocks(kd, vd, to_dev(pairs))
+            kc, vc = oracle.copy_blocks(kc, vc, pairs)
+            n_pairs += len(pairs)
+        write(rand_rows(len(slots)), rand_rows(len(slots)), slots)
+    # round 0 clones the shared partial last blocks: 15 (2040 tokens), 3 (333) and 1 (17)
+    assert n_pairs == 15 + 3 + 1
+    B = len(tables)
+    bt = np.zeros((B, max_blocks), np.int32)
+    for i, t in enumerate(tables):
+        bt[i, :len(t)] = t
+    sl = np.asarray(lens, np.int32)
+    assert pa.pa_validate_decode(bt, sl, bs, nb)[0] == pa.PA_OK
+    q = W.bf16_from_f32(rng.standard_normal((B, Hq, D), dtype=np.float32))
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    pa.pa_decode(out, to_dev(q), kd, vd, to_dev(bt), to_dev(sl), scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(kd), kc) and np.array_equal(to_host(vd), vc)
+    ref = oracle.decode(q, kc, vc, bt, sl, scale)
+    err = max_err(out.cpu().numpy(), ref)
+    note(f"  allocator-driven decode: B={B} max abs err {err:.3e}")
+    assert err <= TOL[W.BF16]
+
+
 def test_reshape_and_cache_every_token_of_config2_bit_exact(pa, oracle):
     wl = W.config(2, keep_logical=True)
     bs = wl.block_size

@@ -48,7 +48,7 @@ def test_valid_step_still_matches_the_oracle(pa, oracle):
         torch.cuda.synchronize()
         ref, kc, _ = oracle_step(oracle, wl)
         assert max_err(dw.out.cpu().numpy(), ref) <= TOL[wl.dtype]
-        assert np.array_equal(to_host(dw.k), kc)
+        assert np.array_equal(to_host(dw.k).view(np.uint8), kc.view(np.uint8))   # bits (NaN poison)
 
 
 def test_duplicate_slots_are_reported_and_nothing_is_written(pa):
