@@ -118,6 +118,22 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, 
                                  int32_t max_blocks, int32_t kv_dtype);
 
 /*
+ * pa_decode_noalloc -- pa_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). It allocates nothing either: the partial softmax states live in
+ * a scratch array of 16 MiB that the library holds on each device until the process ends
+ * (its address is looked up on the first call on a device). Arguments, results and errors
+ * as for pa_decode; sizes whose pa_decode_workspace_bytes exceeds 16 MiB return
+ * PA_ERR_INVALID_ARG (use pa_decode with a workspace). Every call on one device shares
+ * that device's scratch, so calls that overlap on one device (several streams or host
+ * threads) race: serialise them. The scratch needs no initialisation.
+ */
+int32_t pa_decode_noalloc(float* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                          int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                          int32_t max_blocks, float scale, int32_t kv_dtype, void* stream);
+
+/*
  * Tokens per partition that pa_decode uses for these sizes (a sequence longer than this
  * is split into partitions whose partial softmax results are combined exactly).
  */

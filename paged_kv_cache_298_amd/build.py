@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libpa.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
-HIP_SOURCES = ["pa_decode.hip", "pa_multi.hip", "pa_cache.hip"]
+HIP_SOURCES = ["pa_decode.hip", "pa_multi.hip", "pa_cache.hip", "pa_noalloc.hip"]
 HOST_SOURCES = ["pa_api.cpp", "allocator.cpp", "prefix_cache.cpp", "validate.cpp"]
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -360,6 +360,32 @@ int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_
 }
 
 
+int32_t pa_decode_noalloc(float* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                          int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                          int32_t max_blocks, float scale, int32_t kv_dtype, void* stream) {
+    // the scratch pa_decode would need for these sizes (0: none, or sizes it rejects)
+    const size_t need = pa_decode_workspace_bytes(B, Hq, Hkv, D, block_size, max_blocks, kv_dtype);
+    if (need > pa_internal::kScratchBytes)
+        return fail(PA_ERR_INVALID_ARG,
+                    "pa_decode_noalloc: these sizes need %zu bytes of scratch; the library holds %zu per "
+                    "device (use pa_decode with a workspace)", need, pa_internal::kScratchBytes);
+    void* scratch = nullptr;
+    if (need > 0) {
+        const char* err = "";
+        const int e = pa_internal::scratch_pointer(&scratch, &err);
+        if (e != 0) return fail(PA_ERR_HIP, "pa_decode_noalloc: scratch address: %s (%d)", err, e);
+    }
+    const int32_t st = pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, B, Hq, Hkv, D, block_size,
+                                 num_blocks, max_blocks, scale, kv_dtype, scratch,
+                                 need > 0 ? pa_internal::kScratchBytes : 0, stream);
+    if (st != PA_OK) {
+        const std::string msg = g_last_error;
+        return fail(st, "pa_decode_noalloc -> %s", msg.c_str());
+    }
+    return ok();
+}
+
 size_t pa_decode_shared_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t block_size,
                                         int32_t max_blocks, int32_t max_shared_tokens) {
     if (B <= 0 || Hq <= 0 || D <= 0 || block_size <= 0 || max_blocks <= 0 || max_shared_tokens < 0)

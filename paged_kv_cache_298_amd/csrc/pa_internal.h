@@ -116,6 +116,11 @@ constexpr int kMultiMinPart = PA_MULTI_MIN_PART;     // ... but not below this m
 // a HIP error code when the device cannot be queried.
 int stream_waves(int32_t override_waves, int32_t* nw);
 
+// Scratch of pa_decode_noalloc: a device array of kScratchBytes per GPU held by the
+// library (pa_noalloc.hip); scratch_pointer gives its address on the current device.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+int scratch_pointer(void** ptr, const char** err);
+
 // Each returns 0 on success or a nonzero HIP error code (message in *err).
 int launch_decode(const DecodeLaunch& a, const char** err);
 int launch_decode_shared(const SharedLaunch& a, const char** err);

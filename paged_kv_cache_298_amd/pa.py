@@ -28,6 +28,8 @@ _P32 = ctypes.POINTER(ctypes.c_int32)
 _SIGS = {
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _f32, _i32, _vp, _sz, _vp]),
+    "pa_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                 _i32, _f32, _i32, _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_partition_tokens": (_i32, [_i32, _i32]),
     "pa_set_partition_tokens": (_i32, [_i32]),
@@ -159,6 +161,16 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, workspace
     _check(_lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                           _ptr(seq_lens), B, Hq, Hkv, D, bs, nb, max_blocks, float(scale),
                           _kv_dtype(k_cache), _ptr(workspace), ws_bytes, _stream(q, stream)))
+    return out
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, scale, stream=None):
+    """pa_decode on the library's per-device scratch: no workspace, nothing allocated."""
+    B, Hq, D = q.shape
+    nb, Hkv, bs, _ = k_cache.shape
+    _check(_lib.pa_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                  _ptr(seq_lens), B, Hq, Hkv, D, bs, nb, block_tables.shape[1],
+                                  float(scale), _kv_dtype(k_cache), _stream(q, stream)))
     return out
 
 
