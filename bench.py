@@ -1,8 +1,10 @@
 """Benchmark: one decode step of paged attention on one MI355X.
 
 A step is the whole hot path over one batch: clone shared blocks (copy_blocks, when the
-workload has copy-on-write pairs), write each sequence's newest K/V (reshape_and_cache),
-then paged decode attention (pa_decode: stream decode kernel + split-row merge). Inputs
+workload has copy-on-write pairs), then pa_decode_append, which writes each sequence's
+newest K/V to its slot (the reshape_and_cache step) and runs paged decode attention over
+the batch in one launch (stream decode kernel + split-row merge). The same step as separate
+launches (reshape_and_cache, then pa_decode) is timed too, for context. Inputs
 are seeded synthetic data resident in HBM before timing starts; successive steps rotate
 over R replicas of (pool, q, tables, ...) so the working set exceeds the 256 MB Infinity
 Cache. Prints ONE JSON line.
@@ -460,6 +462,14 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(r):
+        # one decode step: the clones (when the batch has copy-on-write pairs), then the
+        # newest tokens' cache write and the decode in one launch
+        if r["pairs"] is not None:
+            pa.pa_copy_blocks(r["k"], r["v"], r["pairs"], stream=stream)
+        pa.pa_decode_append(r["out"], r["q"], r["k"], r["v"], r["nk"], r["nv"], r["slots"], r["bt"],
+                            r["sl"], wl.scale, workspace=r["ws"], stream=stream)
+
+    def step_two_launches(r):
         if r["pairs"] is not None:
             pa.pa_copy_blocks(r["k"], r["v"], r["pairs"], stream=stream)
         pa.pa_reshape_and_cache(r["k"], r["v"], r["nk"], r["nv"], r["slots"], stream=stream)
@@ -484,6 +494,17 @@ def main():
     wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
     ms_step = ev0.elapsed_time(ev1) / args.steps
     _log(f"step: {ms_step * 1e3:.1f} us (events), {wall_ms * 1e3:.1f} us (wall)")
+    # the same step as separate launches (pa_reshape_and_cache, then pa_decode), for context
+    for i in range(args.warmup):
+        step_two_launches(reps[i % R])
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step_two_launches(reps[i % R])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us_two = ev0.elapsed_time(ev1) / args.steps * 1e3
+    _log(f"step as separate cache-write and decode launches: {us_two:.1f} us")
 
     # ---- pa_decode alone: events around every call, on its stream; at least 200 calls
     # after at least 30 warm-up calls, so the mean and percentiles are stable
@@ -559,7 +580,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": W.CONFIG_NAMES[args.config], "global_batch": wl.B,
                    "kv_bytes_per_step": kv_bytes, "replicas_rotated": R,
-                   "step": "copy_blocks (if CoW pairs) + reshape_and_cache + pa_decode"},
+                   "step": "copy_blocks (if CoW pairs) + pa_decode_append (cache write + decode, one launch)",
+                   "us_per_step_separate_launches": round(us_two, 2)},
         "roofline": {"bound": "hbm", "kernel": "pa_decode (decode kernel + split-row merge)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

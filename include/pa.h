@@ -118,6 +118,32 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, 
                                  int32_t max_blocks, int32_t kv_dtype);
 
 /*
+ * pa_decode_append -- one decode step in one launch: the cache write of each sequence's
+ * newest token (pa_reshape_and_cache with T = B) and pa_decode over the batch that
+ * includes it ([P4] section 1, the decode phase: each new token's K/V joins the cache and
+ * the token attends to it; reading [P4] section 1 as in pa_decode, position L_b - 1 is the
+ * newest token and is attended).
+ *
+ *   key, value    device [B, Hkv, D], kv_dtype: the newest token's K and V rows
+ *   slot_mapping  device int32 [B]: the slot of sequence b's newest token, i.e. the slot
+ *                 of its position seq_lens[b] - 1 (table[(L-1) / bs] * bs + (L-1) % bs),
+ *                 or < 0 for a sequence with no new token (its position L - 1 is then
+ *                 read from the cache); distinct
+ *   k_cache, v_cache are written (the given slots) and read
+ * Every other argument, the workspace and the errors as for pa_decode. The result, caches
+ * and output alike, is that of pa_reshape_and_cache followed by pa_decode: on the stream
+ * decomposition one launch writes the rows and reads position L - 1 from key / value, so no
+ * wavefront reads a slot written in the same launch; otherwise the cache write is its own
+ * kernel, launched first. A slot that breaks the precondition gives wrong rows for its
+ * sequence (the debug validation pass reports it as PA_BAD_APPEND_SLOT).
+ */
+int32_t pa_decode_append(float* out, const void* q, void* k_cache, void* v_cache, const void* key,
+                         const void* value, const int32_t* slot_mapping, const int32_t* block_tables,
+                         const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                         int32_t block_size, int32_t num_blocks, int32_t max_blocks, float scale,
+                         int32_t kv_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_noalloc -- pa_decode without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation). It allocates nothing either: the partial softmax states live in
@@ -290,6 +316,7 @@ int32_t pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
 #define PA_DST_IS_SRC 0x40        /* a destination block is also some pair's source */
 #define PA_BAD_GROUP 0x80         /* pa_decode_shared groups break their preconditions */
 #define PA_BAD_QUERY_STARTS 0x100 /* pa_decode_multi q_starts break their preconditions */
+#define PA_BAD_APPEND_SLOT 0x200  /* pa_decode_append: a given slot is not where position L_b - 1 lives */
 
 /*
  * Debug mode, process-wide (default off; PA_VALIDATE=1 in the environment when the
@@ -321,6 +348,9 @@ int32_t pa_validate_groups(const int32_t* groups, int32_t n_groups, const int32_
                            uint32_t* flags);
 int32_t pa_validate_query_starts(const int32_t* q_starts, const int32_t* seq_lens, int32_t B,
                                  int32_t total_q, int32_t max_q, uint32_t* flags);
+int32_t pa_validate_append(const int32_t* slot_mapping, const int32_t* block_tables,
+                           const int32_t* seq_lens, int32_t B, int32_t block_size, int32_t num_blocks,
+                           int32_t max_blocks, uint32_t* flags);
 
 /* ------------------------------------------------------------------ read-ceiling aid */
 

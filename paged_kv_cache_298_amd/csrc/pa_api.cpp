@@ -257,11 +257,15 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, 
     return workspace_layout(B, Hq, D, n_parts_for(block_size, max_blocks), &ml);
 }
 
-int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
-                  const int32_t* block_tables, const int32_t* seq_lens, int32_t B, int32_t Hq,
-                  int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
-                  int32_t max_blocks, float scale, int32_t kv_dtype, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+// pa_decode, and pa_decode_append when nkey != nullptr (the newest token's rows nkey /
+// nval [B, Hkv, D] and slots nslots [B] are written to the cache by the same launch on the
+// stream decomposition, or by the cache-write kernel just before it otherwise).
+static int32_t decode_entry(float* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                            int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                            int32_t max_blocks, float scale, int32_t kv_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream, const void* nkey, const void* nval,
+                            const int32_t* nslots) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0 ||
         max_blocks <= 0)
         return fail(PA_ERR_INVALID_ARG,
@@ -327,6 +331,16 @@ int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_
     a.out = out;
     char* ws = static_cast<char*>(workspace);
     const bool strm = path == pa_internal::kPathStream;
+    a.nkey = strm ? nkey : nullptr;
+    a.nval = strm ? nval : nullptr;
+    a.nslots = strm ? nslots : nullptr;
+    if (nkey && !strm) {   // the cache write as its own kernel, then the decode
+        const char* err = "";
+        const int e = pa_internal::launch_reshape_and_cache(const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                                                            nkey, nval, nslots, B, Hkv, D * elt_bytes(kv_dtype),
+                                                            block_size, num_blocks, stream, &err);
+        if (e != 0) return fail(PA_ERR_HIP, "pa_decode: cache-write launch failed: %s (%d)", err, e);
+    }
     a.ws_o = (!strm && need) ? reinterpret_cast<float*>(ws) : nullptr;
     a.ws_ml = (!strm && need) ? reinterpret_cast<float*>(ws + ml_off) : nullptr;
     a.path = path;
@@ -359,6 +373,43 @@ int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_
     return ok();
 }
 
+
+int32_t pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                  int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+                  int32_t max_blocks, float scale, int32_t kv_dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    return decode_entry(out, q, k_cache, v_cache, block_tables, seq_lens, B, Hq, Hkv, D, block_size,
+                        num_blocks, max_blocks, scale, kv_dtype, workspace, workspace_bytes, stream,
+                        nullptr, nullptr, nullptr);
+}
+
+int32_t pa_decode_append(float* out, const void* q, void* k_cache, void* v_cache, const void* key,
+                         const void* value, const int32_t* slot_mapping, const int32_t* block_tables,
+                         const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                         int32_t block_size, int32_t num_blocks, int32_t max_blocks, float scale,
+                         int32_t kv_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (B > 0 && (!key || !value || !slot_mapping))
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_append: null pointer argument");
+    if (B > 0 && (!aligned(key, 16) || !aligned(value, 16) || !aligned(slot_mapping, 4)))
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_append: misaligned key, value or slot_mapping");
+    if (B > 0 && (int64_t)num_blocks * block_size > 0x7fffffff)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_append: more than 2^31 slots");
+    if (B > 0 && pa_internal::validation_on() && elt_bytes(kv_dtype) != 0 && block_size > 0 && num_blocks > 0 &&
+        max_blocks > 0) {
+        const int32_t st = pa_internal::validate_append_device(slot_mapping, block_tables, seq_lens, B, block_size,
+                                                               num_blocks, max_blocks, stream);
+        if (st != PA_OK) return st;
+    }
+    const int32_t st = decode_entry(out, q, k_cache, v_cache, block_tables, seq_lens, B, Hq, Hkv, D, block_size,
+                                    num_blocks, max_blocks, scale, kv_dtype, workspace, workspace_bytes, stream,
+                                    B > 0 ? key : nullptr, value, slot_mapping);
+    if (st != PA_OK) {
+        const std::string msg = g_last_error;
+        return fail(st, "pa_decode_append -> %s", msg.c_str());
+    }
+    return ok();
+}
 
 int32_t pa_decode_noalloc(float* out, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, const int32_t* seq_lens, int32_t B, int32_t Hq,

@@ -268,7 +268,11 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(Params p) {
 // the per-sequence prefix of group counts kept in LDS, then gathers its table entry.
 // SPLIT: blocks of 8 tokens, so a 16-token group spans two physical blocks; each group
 // then has two tile offsets (tokens 0-7 and 8-15) and K lanes / V loads pick theirs.
-template <int D, int G, int DEPTH, bool SPLIT, bool MULTI, bool DIST>
+// FUSED (pa_decode_append): the batch's newest tokens are also written to their slots by
+// this launch (the reshape_and_cache step); the lanes that would read position L - 1 of a
+// sequence with a new token read it from the input rows instead, so no wave reads a slot
+// written in the same launch and the result is that of the write followed by the decode.
+template <int D, int G, int DEPTH, bool SPLIT, bool MULTI, bool DIST, bool FUSED = false>
 __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
     constexpr int ROW = D * 2;              // bytes per cached row
     constexpr int NQ = D / 32;              // 16-byte registers per ring item
@@ -291,12 +295,40 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
     extern __shared__ int lds_prefix[];
     int* Cs = lds_prefix;           // [B + 1] exclusive prefix of groups per sequence
     int* Ls = lds_prefix + p.B + 1; // [B] lengths clamped into the table's capacity
+    int* Ns = Ls + p.B;             // FUSED: [B] 1 when the sequence's newest token is given
     __shared__ int wsum[4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int cap = p.max_blocks * p.bs;
+
+    // FUSED: the cache write. (sequence, KV head) row r of the new tokens goes to its slot,
+    // rows gw, gw + nw, ... per wave (lanes 0 .. ROW/16-1 move K, the next ROW/16 lanes V).
+    // The first row's load is issued here, beside the lengths' loads, and stored once they
+    // are in, so the write adds no round trip ahead of the first K/V tile.
+    constexpr int UR = ROW / 16;
+    const int gw0 = blockIdx.x * 4 + wid;
+    const bool cw_lane = lane < 2 * UR;
+    const bool cw_v = lane >= UR;
+    const int cw_u = cw_v ? lane - UR : lane;
+    // the destination of row r, whose sequence's slot is sl (-1: no write)
+    auto cw_dst = [&](int r, int sl) -> int64_t {
+        const int g = r - (r / p.Hkv) * p.Hkv;
+        if (sl < 0 || (int64_t)sl >= (int64_t)p.num_blocks * p.bs) return -1;
+        return (((int64_t)(sl >> p.bs_shift) * p.Hkv + g) * p.bs + (sl & (p.bs - 1))) * ROW + cw_u * 16;
+    };
+    auto cw_src = [&](int r) -> const u32x4_t* {
+        return reinterpret_cast<const u32x4_t*>((cw_v ? p.nval : p.nkey) + (int64_t)r * ROW + cw_u * 16);
+    };
+    u32x4_t cw_x = {0u, 0u, 0u, 0u};
+    int cw_sl = -1;
+    if constexpr (FUSED) {
+        if (gw0 < p.B * p.Hkv && cw_lane) {   // loads only: their values are used after the prefix
+            cw_sl = p.nslots[gw0 / p.Hkv];
+            cw_x = *cw_src(gw0);
+        }
+    }
 
     // ---- groups per sequence and their exclusive prefix over the batch (whole block)
     const int per = (p.B + 255) >> 8;
@@ -305,6 +337,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
         const int bb = tid * per + i;
         if (bb < p.B) {
             int L = p.lens[bb];
+            const int nsl = FUSED ? p.nslots[bb] : -1;   // loaded beside the length
             L = L < 0 ? 0 : (L > cap ? cap : L);
             if constexpr (MULTI) {
                 int qs_, n_;
@@ -312,6 +345,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
                 L = n_ > 0 ? L : 0;
             }
             Ls[bb] = L;
+            if constexpr (FUSED) Ns[bb] = (L > 0 && nsl >= 0) ? 1 : 0;
             loc += (L + 15) >> 4;
         }
     }
@@ -334,6 +368,19 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
     }
     if (tid == 255) Cs[p.B] = run;
     __syncthreads();
+    if constexpr (FUSED) {
+        char* cw_cache = const_cast<char*>(cw_v ? p.v : p.k);
+        if (gw0 < p.B * p.Hkv && cw_lane) {
+            const int64_t d = cw_dst(gw0, cw_sl);
+            if (d >= 0) *reinterpret_cast<u32x4_t*>(cw_cache + d) = cw_x;
+        }
+        for (int r = gw0 + p.nw; r < p.B * p.Hkv; r += p.nw) {   // more rows than waves
+            if (cw_lane) {
+                const int64_t d = cw_dst(r, p.nslots[r / p.Hkv]);
+                if (d >= 0) *reinterpret_cast<u32x4_t*>(cw_cache + d) = *cw_src(r);
+            }
+        }
+    }
 
     const int T = __builtin_amdgcn_readfirstlane(Cs[p.B]) * p.Hkv;
     const int gw = blockIdx.x * 4 + wid;
@@ -364,6 +411,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
     uint32_t w_lo = 0, w_hi = 0;   // byte offset of the group's tile in either cache
     uint32_t w_lo1 = 0, w_hi1 = 0; // SPLIT: offset of the tile holding tokens 8-15
     int w_row = 0, w_j = 0;        // its row (b * Hkv + g) and group within the row
+    int w_new = 0;                 // FUSED: 16 + (L - 1) % 16 when the group holds a given
+                                   // newest token at position L - 1, else 0
     int sw = s0;
     auto window = [&](int base) {
         int s = base + lane;
@@ -396,6 +445,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
         }
         w_row = lo * p.Hkv + g;
         w_j = j;
+        if constexpr (FUSED) w_new = (Ns[lo] != 0 && j == n - 1) ? 16 + ((Ls[lo] - 1) & 15) : 0;
     };
     window(sw);
 
@@ -514,9 +564,17 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
             const char* kb1 = p.k + tile_off1(gq);
             kb = khi ? kb1 : kb;
         }
+        kb += koff;
+        if constexpr (FUSED) {   // the lanes of a given newest token read the input row
+            const int nw_info = __builtin_amdgcn_readlane(w_new, s - sw);
+            if (nw_info != 0) {   // wave-uniform, a row's last group only; no load inside
+                const char* in = p.nkey + (int64_t)row * ROW + r * 16;
+                kb = ktok == nw_info - 16 ? in : kb;
+            }
+        }
 #pragma unroll
         for (int k = 0; k < NQ; ++k)
-            dst.q[k] = kv_load16(reinterpret_cast<const u32x4_t*>(kb + koff + k * 64));
+            dst.q[k] = kv_load16(reinterpret_cast<const u32x4_t*>(kb + k * 64));
     };
     // V load k holds rows r + 4k; with SPLIT, loads 2 and 3 (rows 8-15) read the second
     // block at rows r + 4 (k - 2)
@@ -525,9 +583,20 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
         const char* vb1 = vb + 2 * 4 * ROW;
         if constexpr (SPLIT) vb1 = p.v + tile_off1(gq);
         // address of V load k (rows r + 4k of the group)
-        auto vaddr = [&](int k) -> const char* {
-            return k < 2 ? vb + voff + k * 4 * ROW : vb1 + voff + (k - 2) * 4 * ROW;
-        };
+        const char* va[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) va[k] = k < 2 ? vb + voff + k * 4 * ROW : vb1 + voff + (k - 2) * 4 * ROW;
+        if constexpr (FUSED) {   // the lanes of a given newest token read the input row
+            int sv = s0 + gq;
+            sv = sv < s1 ? sv : s1 - 1;
+            const int nw_info = __builtin_amdgcn_readlane(w_new, sv - sw);
+            if (nw_info != 0) {   // wave-uniform, a row's last group only; no load inside
+                const char* vin = p.nval + (int64_t)__builtin_amdgcn_readlane(w_row, sv - sw) * ROW + c * WV;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) va[k] = r + 4 * k == nw_info - 16 ? vin : va[k];
+            }
+        }
+        auto vaddr = [&](int k) -> const char* { return va[k]; };
         if constexpr (WV == 16) {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
@@ -990,10 +1059,10 @@ int stream_shape(size_t need_lds, int* nw, size_t* lds) {
     return 0;
 }
 
-template <int D, int G, bool SPLIT, bool MULTI = false, bool DIST = false>
+template <int D, int G, bool SPLIT, bool MULTI = false, bool DIST = false, bool FUSED = false>
 hipError_t launch_stream(Params prm, int nw_req, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    size_t lds = (size_t)(2 * prm.B + 1) * sizeof(int);
+    size_t lds = (size_t)((FUSED ? 3 : 2) * prm.B + 1) * sizeof(int);
     int nw = 0;
     const int e = stream_shape(lds, &nw, &lds);
     if (e != 0) return (hipError_t)e;
@@ -1001,20 +1070,26 @@ hipError_t launch_stream(Params prm, int nw_req, void* stream) {
     nw = nw > pa_internal::kMaxStreamWaves ? pa_internal::kMaxStreamWaves : nw;
     nw = (nw + 3) / 4 * 4;
     prm.nw = nw;
-    hipLaunchKernelGGL((decode_stream_kernel<D, G, PA_STREAM_DEPTH, SPLIT, MULTI, DIST>), dim3(nw / 4), dim3(256), lds, s, prm);
+    hipLaunchKernelGGL((decode_stream_kernel<D, G, PA_STREAM_DEPTH, SPLIT, MULTI, DIST, FUSED>), dim3(nw / 4), dim3(256), lds, s, prm);
     hipLaunchKernelGGL((stream_reduce_kernel<D, G, MULTI>), dim3(nw), dim3(256), 0, s, prm);
     return hipGetLastError();
 }
 
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool FUSED>
 hipError_t dispatch_stream_g(const Params& prm, int G, int nw, void* stream) {
     switch (G) {
-        case 1: return launch_stream<D, 1, SPLIT>(prm, nw, stream);
-        case 2: return launch_stream<D, 2, SPLIT>(prm, nw, stream);
-        case 4: return launch_stream<D, 4, SPLIT>(prm, nw, stream);
-        case 8: return launch_stream<D, 8, SPLIT, false, (PA_STREAM_DIST8 != 0)>(prm, nw, stream);
+        case 1: return launch_stream<D, 1, SPLIT, false, false, FUSED>(prm, nw, stream);
+        case 2: return launch_stream<D, 2, SPLIT, false, false, FUSED>(prm, nw, stream);
+        case 4: return launch_stream<D, 4, SPLIT, false, false, FUSED>(prm, nw, stream);
+        case 8: return launch_stream<D, 8, SPLIT, false, (PA_STREAM_DIST8 != 0), FUSED>(prm, nw, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <int D, bool FUSED>
+hipError_t dispatch_stream_split(const Params& prm, int G, int nw, bool split, void* stream) {
+    return split ? dispatch_stream_g<D, true, FUSED>(prm, G, nw, stream)
+                 : dispatch_stream_g<D, false, FUSED>(prm, G, nw, stream);
 }
 
 template <bool BF16, int D>
@@ -1084,11 +1159,18 @@ int launch_decode(const DecodeLaunch& a, const char** err) {
     hipError_t e;
     if (a.path == kPathStream) {
         const bool split = a.bs < 16;
-        e = a.D == 64 ? (split ? dispatch_stream_g<64, true>(prm, G, a.stream_waves, a.stream)
-                               : dispatch_stream_g<64, false>(prm, G, a.stream_waves, a.stream))
-          : a.D == 128 ? (split ? dispatch_stream_g<128, true>(prm, G, a.stream_waves, a.stream)
-                                : dispatch_stream_g<128, false>(prm, G, a.stream_waves, a.stream))
-                       : hipErrorInvalidValue;
+        const bool fused = a.nkey != nullptr;
+        prm.nkey = static_cast<const char*>(a.nkey);
+        prm.nval = static_cast<const char*>(a.nval);
+        prm.nslots = a.nslots;
+        if (a.D == 64)
+            e = fused ? dispatch_stream_split<64, true>(prm, G, a.stream_waves, split, a.stream)
+                      : dispatch_stream_split<64, false>(prm, G, a.stream_waves, split, a.stream);
+        else if (a.D == 128)
+            e = fused ? dispatch_stream_split<128, true>(prm, G, a.stream_waves, split, a.stream)
+                      : dispatch_stream_split<128, false>(prm, G, a.stream_waves, split, a.stream);
+        else
+            e = hipErrorInvalidValue;
     } else {
         e = a.kv_dtype == 1 ? dispatch_d<true>(prm, a.B, a.Hkv, a.D, G, a.stream)
                             : dispatch_d<false>(prm, a.B, a.Hkv, a.D, G, a.stream);

@@ -90,6 +90,11 @@ struct Params {
     int pre_items;           // prefix items (group, KV head, partition) of a fused launch
     int pre_blocks;          // blocks holding them, four items each
     int suf_items;           // suffix partitions of a fused launch
+    // fused cache write (pa_decode_append) only: the newest token of every sequence, K and
+    // V rows [B, Hkv, D], and its slot (< 0: none); read from here for position L - 1
+    const char* nkey;
+    const char* nval;
+    const int32_t* nslots;
     // multi-query mode only (q_starts == nullptr otherwise)
     const int32_t* q_starts; // [B + 1] offsets of each sequence's queries in q
     int total_q;             // query tokens in q (host value the device offsets are clamped to)

@@ -31,6 +31,11 @@ struct DecodeLaunch {
     int32_t* meta;           // [4]
     int32_t stream_waves;    // 0 = every wave the device holds at once
     int32_t min_slice;       // fewest 16-token groups per wave
+    // pa_decode_append on the stream decomposition: the newest token's K and V rows
+    // [B, Hkv, D] and slots [B], written by the decode launch itself (nkey == nullptr: none)
+    const void* nkey;
+    const void* nval;
+    const int32_t* nslots;
 };
 
 constexpr int kMaxPartTokens = 1024;
@@ -151,6 +156,8 @@ int32_t validate_multi_device(const int32_t* tables, const int32_t* lens, const 
 int32_t validate_slots_device(const int32_t* slots, int32_t T, int32_t block_size, int32_t num_blocks,
                               void* stream);
 int32_t validate_pairs_device(const int32_t* pairs, int32_t N, int32_t num_blocks, void* stream);
+int32_t validate_append_device(const int32_t* slots, const int32_t* tables, const int32_t* lens, int32_t B,
+                               int32_t block_size, int32_t num_blocks, int32_t max_blocks, void* stream);
 // bytes from device memory to host memory on `stream`, waiting for the copy (0 or a HIP
 // error code, message in *err)
 int copy_to_host(void* dst, const void* src, size_t bytes, void* stream, const char** err);

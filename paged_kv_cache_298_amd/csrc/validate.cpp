@@ -92,6 +92,26 @@ void check_slots(Findings& f, const int32_t* slots, int32_t T, int32_t block_siz
                   used[k - 1].second, used[k].second, used[k].first);
 }
 
+// pa_decode_append: a given slot must be where position L - 1 of its sequence lives
+void check_append(Findings& f, const int32_t* slots, const int32_t* tables, const int32_t* lens, int32_t B,
+                  int32_t block_size, int32_t max_blocks) {
+    const int64_t cap = (int64_t)block_size * max_blocks;
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t s = slots[b];
+        if (s < 0) continue;
+        const int32_t L = lens[b];
+        if (L < 1 || L > cap) {
+            f.add(PA_BAD_APPEND_SLOT, "slot_mapping[%d] = %d given for a sequence of %d tokens", b, s, L);
+            continue;
+        }
+        const int32_t pos = L - 1;
+        const int64_t want = (int64_t)tables[(int64_t)b * max_blocks + pos / block_size] * block_size + pos % block_size;
+        if (s != want)
+            f.add(PA_BAD_APPEND_SLOT, "slot_mapping[%d] = %d, but position %d of sequence %d lives in slot %lld",
+                  b, s, pos, b, (long long)want);
+    }
+}
+
 void check_pairs(Findings& f, const int32_t* pairs, int32_t N, int32_t num_blocks) {
     std::vector<std::pair<int32_t, int32_t>> dst;   // (destination, pair)
     std::vector<int32_t> src;
@@ -242,6 +262,20 @@ int32_t validate_slots_device(const int32_t* slots, int32_t T, int32_t block_siz
     return f.finish(who, nullptr);
 }
 
+int32_t validate_append_device(const int32_t* slots, const int32_t* tables, const int32_t* lens, int32_t B,
+                               int32_t block_size, int32_t num_blocks, int32_t max_blocks, void* stream) {
+    const char* who = "pa_decode_append";
+    std::vector<int32_t> s, t, l;
+    int32_t st = fetch(s, slots, B, stream, who);
+    if (st == PA_OK) st = fetch(l, lens, B, stream, who);
+    if (st == PA_OK) st = fetch(t, tables, (int64_t)B * max_blocks, stream, who);
+    if (st != PA_OK) return st;
+    Findings f;
+    check_slots(f, s.data(), B, block_size, num_blocks);
+    check_append(f, s.data(), t.data(), l.data(), B, block_size, max_blocks);
+    return f.finish(who, nullptr);
+}
+
 int32_t validate_pairs_device(const int32_t* pairs, int32_t N, int32_t num_blocks, void* stream) {
     const char* who = "pa_copy_blocks";
     std::vector<int32_t> p;
@@ -284,6 +318,18 @@ int32_t pa_validate_slots(const int32_t* slot_mapping, int32_t T, int32_t block_
     Findings f;
     check_slots(f, slot_mapping, T, block_size, num_blocks);
     return f.finish("pa_validate_slots", flags);
+}
+
+int32_t pa_validate_append(const int32_t* slot_mapping, const int32_t* block_tables,
+                           const int32_t* seq_lens, int32_t B, int32_t block_size, int32_t num_blocks,
+                           int32_t max_blocks, uint32_t* flags) {
+    if (B < 0 || block_size <= 0 || num_blocks <= 0 || max_blocks <= 0 ||
+        (B > 0 && (!slot_mapping || !block_tables || !seq_lens)))
+        return pa_internal::set_error(PA_ERR_INVALID_ARG, "pa_validate_append: bad arguments");
+    Findings f;
+    check_slots(f, slot_mapping, B, block_size, num_blocks);
+    check_append(f, slot_mapping, block_tables, seq_lens, B, block_size, max_blocks);
+    return f.finish("pa_validate_append", flags);
 }
 
 int32_t pa_validate_block_pairs(const int32_t* block_pairs, int32_t N, int32_t num_blocks,

@@ -28,6 +28,8 @@ _P32 = ctypes.POINTER(ctypes.c_int32)
 _SIGS = {
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _f32, _i32, _vp, _sz, _vp]),
+    "pa_decode_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _f32, _i32, _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
@@ -52,6 +54,7 @@ _SIGS = {
     "pa_validate_block_pairs": (_i32, [_vp, _i32, _i32, _vp]),
     "pa_validate_groups": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_validate_query_starts": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
+    "pa_validate_append": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "pa_status_string": (ctypes.c_char_p, [_i32]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_abi_version": (_i32, []),
@@ -83,6 +86,7 @@ EXPORTS = tuple(_SIGS)
 # flags of the debug validation pass (include/pa.h)
 PA_BAD_LENGTH, PA_BAD_TABLE_ENTRY, PA_BAD_SLOT, PA_DUP_SLOT = 0x1, 0x2, 0x4, 0x8
 PA_BAD_PAIR, PA_DUP_DST, PA_DST_IS_SRC, PA_BAD_GROUP, PA_BAD_QUERY_STARTS = 0x10, 0x20, 0x40, 0x80, 0x100
+PA_BAD_APPEND_SLOT = 0x200
 
 
 class PaError(RuntimeError):
@@ -161,6 +165,26 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, workspace
     _check(_lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                           _ptr(seq_lens), B, Hq, Hkv, D, bs, nb, max_blocks, float(scale),
                           _kv_dtype(k_cache), _ptr(workspace), ws_bytes, _stream(q, stream)))
+    return out
+
+
+def pa_decode_append(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables, seq_lens,
+                     scale, workspace=None, stream=None):
+    """One decode step: write each sequence's newest K/V row (key/value [B, Hkv, D]) to its slot
+    (slot_mapping int32 [B]: the slot of position seq_lens[b] - 1, or < 0 for none) and run
+    pa_decode over the batch including it; the same result as pa_reshape_and_cache followed by
+    pa_decode."""
+    B, Hq, D = q.shape
+    nb, Hkv, bs, _ = k_cache.shape
+    max_blocks = block_tables.shape[1]
+    need = pa_decode_workspace_bytes(B, Hq, Hkv, D, bs, max_blocks, _kv_dtype(k_cache))
+    if workspace is None and need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.pa_decode_append(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value),
+                                 _ptr(slot_mapping), _ptr(block_tables), _ptr(seq_lens), B, Hq, Hkv, D, bs,
+                                 nb, max_blocks, float(scale), _kv_dtype(k_cache), _ptr(workspace),
+                                 ws_bytes, _stream(q, stream)))
     return out
 
 
@@ -427,6 +451,14 @@ def pa_validate_groups(groups, block_tables, seq_lens, block_size, max_members, 
     return _validate(_lib.pa_validate_groups, gp, int(g.reshape(-1, 3).shape[0]), tp, lp,
                      int(t.shape[0]), int(block_size), int(t.shape[1]), int(max_members),
                      int(max_shared_tokens))
+
+
+def pa_validate_append(slot_mapping, block_tables, seq_lens, block_size, num_blocks):
+    s_, sp = _host_i32(slot_mapping)
+    t, tp = _host_i32(block_tables)
+    l, lp = _host_i32(seq_lens)
+    return _validate(_lib.pa_validate_append, sp, tp, lp, int(t.shape[0]), int(block_size), int(num_blocks),
+                     int(t.shape[1]))
 
 
 def pa_validate_query_starts(q_starts, seq_lens, max_q):

@@ -116,6 +116,19 @@ def test_shared_groups_and_query_offsets_are_checked(pa):
                                                    wm.scale), "sequence 1")
 
 
+def test_append_slot_off_the_newest_position_is_reported(pa):
+    wl = W.config(2)
+    dw = DevWorkload(wl)
+    dw.out.fill_(7.0)
+    slots = wl.slot_mapping.copy()
+    slots[4] = slots[4] - 1 if slots[4] % 16 else slots[4] + 1   # another slot of the same block
+    note("debug validation: append slot not at position L - 1")
+    _expect_invalid(pa, lambda: pa.pa_decode_append(dw.out, dw.q, dw.k, dw.v, dw.nk, dw.nv, to_dev(slots),
+                                                    dw.bt, dw.sl, wl.scale), "lives in slot")
+    torch.cuda.synchronize()
+    assert (dw.out == 7.0).all()
+
+
 @pytest.mark.parametrize("tile_mult", [1, 2])
 def test_read_tiles_clamps_offsets_into_the_caches(pa, tile_mult):
     """Offsets before the start, past the end and not 16-aligned are clamped into

@@ -102,3 +102,15 @@ def test_validators_reject_bad_arguments():
     assert pa._lib.pa_validate_slots(None, 3, 16, 4, None) == pa.PA_ERR_INVALID_ARG
     assert pa._lib.pa_validate_decode(None, None, 2, 16, 4, 4, None) == pa.PA_ERR_INVALID_ARG
     assert pa._lib.pa_validate_block_pairs(None, 0, 4, None) == pa.PA_OK
+
+
+def test_append_slots_must_hold_the_newest_position():
+    bt = np.array([[3, 4, 9], [5, 6, 0]], np.int32)
+    lens = [20, 16]                          # newest positions 19 (block 4) and 15 (block 5)
+    ok = [4 * 16 + 3, 5 * 16 + 15]
+    assert pa.pa_validate_append(ok, bt, lens, 16, 10)[:2] == (pa.PA_OK, 0)
+    assert pa.pa_validate_append([-1, 5 * 16 + 15], bt, lens, 16, 10)[:2] == (pa.PA_OK, 0)
+    st, flags, msg = pa.pa_validate_append([4 * 16 + 4, 5 * 16 + 15], bt, lens, 16, 10)
+    assert flags == pa.PA_BAD_APPEND_SLOT and "position 19 of sequence 0 lives in slot 67" in msg
+    st, flags, _ = pa.pa_validate_append([7, 7], bt, [0, 16], 16, 10)   # no token at all; duplicate
+    assert flags & pa.PA_BAD_APPEND_SLOT and flags & pa.PA_DUP_SLOT
