@@ -204,6 +204,34 @@ def _sweep_block_size(torch, pa, W, dev, args):
             torch.cuda.empty_cache()
 
 
+def _sweep_group_size(torch, pa, W, dev, args):
+    """The same 64 sequences (lengths of the Llama-3-8B batch, Hkv = 8, D = 128, bs = 16, the
+    same K/V bytes) with G = Hq / Hkv = 1, 2, 4 and 8 query heads per KV head; pa_decode
+    alone, HIP events around each call, two replicas rotated. One JSON line per G."""
+    L = W.config(2, poison=False).seq_lens
+    steps = max(100, min(args.steps, 300))
+    for G in (1, 2, 4, 8):
+        wl = W.make_workload(f"llama3-8b-G{G}", 64, 8 * G, 8, 128, 16, L, W.BF16, 29802,
+                             max_blocks=256, poison=False)
+        ws_bytes = pa.pa_decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, 16, wl.max_blocks, pa.PA_BF16)
+        reps = [dict(q=_to_dev(wl.q, torch, dev), k=_to_dev(wl.k_cache, torch, dev),
+                     v=_to_dev(wl.v_cache, torch, dev), bt=_to_dev(wl.block_tables, torch, dev),
+                     sl=_to_dev(wl.seq_lens, torch, dev),
+                     out=torch.empty((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=dev),
+                     ws=torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev))
+                for _ in range(2)]
+        stream = torch.cuda.current_stream(dev)
+        t = _per_call_us(torch, lambda r: pa.pa_decode(r["out"], r["q"], r["k"], r["v"], r["bt"], r["sl"],
+                                                       wl.scale, workspace=r["ws"], stream=stream),
+                         reps, steps, 30, stream)
+        kv = wl.kv_bytes()
+        print(json.dumps({"sweep": "group_size", "G": G, "Hq": wl.Hq, "Hkv": wl.Hkv, "kv_bytes": kv,
+                          "decode_us": t, "GBps": round(kv / (t["mean"] * 1e-6) / 1e9, 1),
+                          "frac": round(kv / (t["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
+        del reps
+        torch.cuda.empty_cache()
+
+
 def _per_call_us(torch, fn, reps, steps, warmup, stream):
     """Mean, p10, p50 and p90 of fn's duration in us: HIP events around each call on its
     stream, rotating over the replicas."""
@@ -403,6 +431,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run pa_copy_blocks over a known number of bytes (the reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and print them")
+    ap.add_argument("--sweep-group-size", action="store_true",
+                    help="pa_decode on the Llama-3-8B lengths with G = 1, 2, 4, 8 query heads per "
+                         "KV head (same K/V bytes); one JSON line per G")
     ap.add_argument("--read-calibration", action="store_true",
                     help="only run pa_read_tiles (non-temporal loads) over the Llama-3-8B "
                          "batch's tiles, a known number of bytes, and print them")
@@ -427,6 +458,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         _copy_calibration(torch, pa, dev)
+        return
+    if args.sweep_group_size:
+        _sweep_group_size(torch, pa, W, dev, args)
         return
     if args.read_calibration:
         _read_calibration(torch, pa, W, dev)
