@@ -189,6 +189,14 @@ int32_t pa_set_decode_path(int32_t path);
 int32_t pa_set_stream_waves(int32_t waves, int32_t min_slice);
 
 /*
+ * Process-wide order in which pa_decode_multi's query-tile work is handed to the waves,
+ * for tests and sweeps: 1 (default) longest first, 0 the plain grid order (KV head, tile
+ * from the last, partition, sequence). The order changes only which wavefront runs which
+ * piece of work, never the result: both give identical bits. Not thread-safe.
+ */
+int32_t pa_set_multi_order(int32_t longest_first);
+
+/*
  * pa_decode_shared -- pa_decode for a batch in which groups of consecutive sequences
  * share their leading blocks (shared prompts and parallel sampling: [P1] "Shared Prompts"
  * and "Parallel Sampling"; [P2] section 5 "Copy-on-write sharing"). Every shared K/V tile
@@ -245,6 +253,12 @@ size_t pa_decode_shared_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_
  * every other argument as for pa_decode. Offsets that break the preconditions are clamped
  * on the device: wrong rows for the sequences concerned, never an access outside the
  * buffers. Rows of queries no sequence owns are left unwritten.
+ *
+ * Chunks that fit one 16-column score tile per (sequence, KV head) (max_q x Hq / Hkv <= 16,
+ * e.g. draft tokens) run on pa_decode's stream decomposition. Longer ones are cut into
+ * query tiles of up to 64 rows; the tiles see different numbers of tokens (a chunk's
+ * later tiles more, a sequence with more cached tokens more), and the waves take them
+ * longest first (for B <= 2048; pa_set_multi_order).
  */
 int32_t pa_decode_multi(float* out, const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* block_tables, const int32_t* seq_lens,

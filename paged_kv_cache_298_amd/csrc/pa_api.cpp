@@ -18,6 +18,7 @@ int32_t g_partition_override = 0;   // 0 = automatic
 int32_t g_path = PA_PATH_AUTO;
 int32_t g_stream_waves = 0;         // 0 = every wave the device holds at once
 int32_t g_min_slice = pa_internal::kDefaultMinSlice;
+int32_t g_longest_first = 1;
 
 int32_t fail(int32_t status, const char* fmt, ...) {
     char buf[512];
@@ -241,6 +242,14 @@ int32_t pa_set_stream_waves(int32_t waves, int32_t min_slice) {
                     pa_internal::kMaxStreamWaves, waves, min_slice);
     g_stream_waves = waves;
     g_min_slice = min_slice == 0 ? pa_internal::kDefaultMinSlice : min_slice;
+    return ok();
+}
+
+int32_t pa_set_multi_order(int32_t longest_first) {
+    if (longest_first != 0 && longest_first != 1)
+        return fail(PA_ERR_INVALID_ARG, "multi order must be 0 (grid order) or 1 (longest first), got %d",
+                    longest_first);
+    g_longest_first = longest_first;
     return ok();
 }
 
@@ -631,6 +640,7 @@ int32_t pa_decode_multi(float* out, const void* q, const void* k_cache, const vo
     a.n_tiles = pl.n_tiles;
     a.part_tokens = pl.part_tokens;
     a.n_parts = pl.n_parts;
+    a.longest_first = g_longest_first;
     a.stream_g = stream_g;
     a.rec_o = nullptr;
     a.rec_ml = nullptr;

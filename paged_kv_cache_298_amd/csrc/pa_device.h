@@ -100,6 +100,8 @@ struct Params {
     int total_q;             // query tokens in q (host value the device offsets are clamped to)
     int max_q;               // host bound on queries per sequence
     int n_tiles;             // query tiles per (sequence, KV head)
+    int lpt_buckets;         // work classes of the longest-first order (0: grid order)
+    int lpt_shift;           // log2 of the tokens per work class
 };
 
 // Shared-prefix mode: the tokens sequence b shares with its group (groups are sorted by

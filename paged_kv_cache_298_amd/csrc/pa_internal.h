@@ -86,6 +86,7 @@ struct MultiLaunch {
     int32_t B, total_q, max_q, Hq, Hkv, D, bs, num_blocks, max_blocks;
     int32_t nset;            // query tile = 16 nset rows
     int32_t n_tiles, part_tokens, n_parts;
+    int32_t longest_first;   // query-tile work handed out longest first (else grid order)
     // stream decomposition (stream_g > 0): the decode kernel's slices with stream_g query
     // columns (token x head) per row instead of query tiles
     int32_t stream_g;

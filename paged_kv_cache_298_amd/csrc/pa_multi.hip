@@ -266,7 +266,7 @@ __device__ __forceinline__ void prefix_item(const Params& p, int id) {
 // A row whose position lies in partition 0 (np = 1) is written normalized; otherwise
 // every partition leaves a record and multi rows are merged by decode_reduce_kernel.
 template <int D, int NSET>
-__device__ __forceinline__ void multi_item(const Params& p, int id) {
+__device__ __forceinline__ void multi_item(const Params& p, int g, int b, int part, int tile) {
     constexpr int ROW = D * 2;
     constexpr int NQ = D / 32;
     constexpr int WV = D / 8;
@@ -276,16 +276,6 @@ __device__ __forceinline__ void multi_item(const Params& p, int id) {
     static_assert(D == 64 || D == 128, "head size");
 
     const int lane = threadIdx.x & 63;
-    // item order: KV head fastest (the heads spread over the XCDs), then query tile from
-    // the last (a chunk's later tiles see the most tokens, so they start first), then
-    // partition, then sequence: the tiles of one (sequence, KV head) run together on one
-    // XCD and share its L2
-    const int g = id % p.Hkv;
-    int rest = id / p.Hkv;
-    const int tile = p.n_tiles - 1 - rest % p.n_tiles;
-    rest /= p.n_tiles;
-    const int part = rest % p.n_parts;
-    const int b = rest / p.n_parts;
     if (b >= p.B) return;
     const int cap = p.max_blocks * p.bs;
     int L = p.lens[b];
@@ -572,11 +562,177 @@ __device__ __forceinline__ void multi_item(const Params& p, int id) {
     }
 }
 
+// Longest-first order of the multi-query work.
+//
+// A unit is (sequence b, token partition part, query tile t); its Hkv items (one per KV
+// head) are adjacent in the grid. Its work is ntok, the tokens of the partition that the
+// tile's last query sees. Waves take units in decreasing ntok, counted in classes of
+// 2^lpt_shift tokens (class k holds ntok in ((k-1)Q, kQ], the last class everything above),
+// and within a class by sequence, then partition, then tile from the last. Longest first
+// keeps a long unit from starting last behind a CU that already ran short ones; the classes
+// keep a sequence's neighbouring tiles together so they share the XCD's L2. The order moves
+// work between waves only: every unit's arithmetic, and so every output bit, is the same
+// in any order.
+//
+// Each block derives the order itself: the per-sequence query counts go to LDS, every
+// (sequence, partition) pair adds its tiles to the class histogram, a scan turns the
+// histogram into class starts, and each wave finds its unit from its rank: the class by a
+// binary search, then the pair by a running count over the pairs in order, then the tile.
+// Tiles of a sequence with n queries after `base` cached tokens see, for tile t,
+// vis(t) = base + (min((t+1) R, n G) - 1) / G + 1 tokens (R = 16 NSET rows per tile);
+// vis increases with t, so the tiles with vis >= y are the last tiles_from(y) ones.
+constexpr int kLptBuckets = 1024;
+constexpr int kLptSeqs = 2048;
+
+__device__ __forceinline__ int tiles_from(int y, int base, int n, int nt, int G, int rshift) {
+    const int d = y - base - 1;
+    if (d < 0) return nt;
+    if (n <= d) return 0;
+    return nt + 1 - ((d * G + (1 << rshift)) >> rshift);   // nt - (ceil((dG + 1) / R) - 1)
+}
+
+// Tiles of pair (b, part) in class k: the last `a` tiles hold ntok > (k-1)Q, the last
+// `c` of those ntok > kQ (c = 0 in the top class).
+__device__ __forceinline__ void class_tiles(int k, int part, int base, int n, int nt, int G, int rshift,
+                                            const Params& p, int* a, int* c) {
+    const int lo = part * p.part_tokens + ((k - 1) << p.lpt_shift);
+    *a = tiles_from(lo + 1, base, n, nt, G, rshift);
+    *c = k < p.lpt_buckets ? tiles_from(lo + (1 << p.lpt_shift) + 1, base, n, nt, G, rshift) : 0;
+}
+
+// The unit of rank `rank` in the longest-first order; false when rank is past the last
+// unit. Every thread of the block calls it (it holds block barriers).
+template <int NSET>
+__device__ bool lpt_unit(const Params& p, int rank, int* b_out, int* part_out, int* tile_out) {
+    __shared__ int2 seq[kLptSeqs];          // (cached tokens before the chunk, queries)
+    __shared__ int hist[kLptBuckets];       // units per class, top class first
+    __shared__ int start[kLptBuckets];      // their exclusive prefix
+    constexpr int rshift = 4 + (NSET == 1 ? 0 : (NSET == 2 ? 1 : 2));
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int G = p.Hq / p.Hkv;
+    const int K = p.lpt_buckets;
+    const int P = p.part_tokens;
+    const int cap = p.max_blocks * p.bs;
+    for (int i = tid; i < K; i += 256) hist[i] = 0;
+    for (int b = tid; b < p.B; b += 256) {
+        int L = p.lens[b];
+        L = L < 0 ? 0 : (L > cap ? cap : L);
+        int qs, n;
+        multi_rows(p, b, L, &qs, &n);
+        seq[b] = make_int2(L - n, n);
+    }
+    __syncthreads();
+    const int NP = p.B * p.n_parts;
+    for (int pr = tid; pr < NP; pr += 256) {
+        const int b = pr / p.n_parts, part = pr - b * p.n_parts;
+        const int base = seq[b].x, n = seq[b].y;
+        const int L = base + n;
+        if (n <= 0 || part * P >= L) continue;
+        const int nt = (n * G + (16 * NSET - 1)) >> rshift;
+        // ntok of the pair's first tile (the one with the fewest tokens) and of its last
+        const int tf = nt - tiles_from(part * P + 1, base, n, nt, G, rshift);
+        const int vf = base + (min((tf + 1) << rshift, n * G) - 1) / G + 1;
+        const int k_lo = (min(vf, (part + 1) * P) - part * P + (1 << p.lpt_shift) - 1) >> p.lpt_shift;
+        const int k_hi = (min(L, (part + 1) * P) - part * P + (1 << p.lpt_shift) - 1) >> p.lpt_shift;
+        for (int k = k_lo; k <= k_hi; ++k) {
+            int a, c;
+            class_tiles(k, part, base, n, nt, G, rshift, p, &a, &c);
+            if (a > c) atomicAdd(&hist[K - k], a - c);
+        }
+    }
+    __syncthreads();
+    if (tid < 64) {
+        // exclusive scan of the histogram: lane i sums a run of slots, the lanes' totals
+        // are scanned across the wave, then each lane writes its run
+        const int per = (K + 63) >> 6;
+        const int s0 = min(lane * per, K), s1 = min(s0 + per, K);
+        int run = 0;
+        for (int s = s0; s < s1; ++s) run += hist[s];
+        int incl = run;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(incl, d);
+            incl += lane >= d ? o : 0;
+        }
+        int acc = incl - run;
+        for (int s = s0; s < s1; ++s) {
+            start[s] = acc;
+            acc += hist[s];
+        }
+    }
+    __syncthreads();
+    const int total = start[K - 1] + hist[K - 1];
+    if (rank >= total) return false;
+    int lo = 0, hi = K - 1;                 // last slot whose start is <= rank
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (start[mid] <= rank) lo = mid;
+        else hi = mid - 1;
+    }
+    const int k = K - lo;
+    int j = rank - start[lo];
+    for (int c0 = 0; c0 < NP; c0 += 64) {
+        const int pr = c0 + lane;
+        int cnt = 0, a = 0, c = 0;
+        if (pr < NP) {
+            const int b = pr / p.n_parts, part = pr - b * p.n_parts;
+            const int base = seq[b].x, n = seq[b].y;
+            if (n > 0 && part * P < base + n) {
+                const int nt = (n * G + (16 * NSET - 1)) >> rshift;
+                class_tiles(k, part, base, n, nt, G, rshift, p, &a, &c);
+                cnt = a > c ? a - c : 0;
+            }
+        }
+        int incl = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(incl, d);
+            incl += lane >= d ? o : 0;
+        }
+        const int sum = __shfl(incl, 63);
+        if (j < sum) {
+            const uint64_t m = __ballot(incl > j);
+            const int w = __builtin_ctzll(m);
+            const int before = __shfl(incl - cnt, w);
+            const int cw = __shfl(c, w);
+            const int prw = c0 + w;
+            const int b = prw / p.n_parts;
+            const int n = seq[b].y;
+            const int nt = (n * G + (16 * NSET - 1)) >> rshift;
+            *b_out = b;
+            *part_out = prw - b * p.n_parts;
+            *tile_out = nt - cw - 1 - (j - before);   // tiles from the last within the class
+            return true;
+        }
+        j -= sum;
+    }
+    return false;
+}
+
 // All multi-query items, four per 256-thread block.
 template <int D, int NSET>
 __global__ __launch_bounds__(256) void decode_multi_kernel(Params p) {
-    const int item = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-    if (item < p.pre_items) multi_item<D, NSET>(p, item);
+    const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (int)(threadIdx.x >> 6));
+    const int g = item % p.Hkv;
+    int b, part, tile;
+    if (p.lpt_buckets > 0) {
+        if (!lpt_unit<NSET>(p, item / p.Hkv, &b, &part, &tile)) return;
+        b = __builtin_amdgcn_readfirstlane(b);
+        part = __builtin_amdgcn_readfirstlane(part);
+        tile = __builtin_amdgcn_readfirstlane(tile);
+    } else {
+        // grid order: KV head fastest (the heads spread over the XCDs), then query tile from
+        // the last (a chunk's later tiles see the most tokens, so they start first), then
+        // partition, then sequence
+        if (item >= p.pre_items) return;
+        int rest = item / p.Hkv;
+        tile = p.n_tiles - 1 - rest % p.n_tiles;
+        rest /= p.n_tiles;
+        part = rest % p.n_parts;
+        b = rest / p.n_parts;
+    }
+    multi_item<D, NSET>(p, g, b, part, tile);
 }
 
 // The prefix partitions and the members' own tokens in one launch of 4-wave blocks, one
@@ -587,7 +743,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(Params p) {
 template <int D, int G, int NSET>
 __global__ __launch_bounds__(256) void decode_shared_kernel(Params p) {
     const int bid = blockIdx.x;
-    const int item = (bid < p.pre_blocks ? bid : bid - p.pre_blocks) * 4 + (int)(threadIdx.x >> 6);
+    const int item = __builtin_amdgcn_readfirstlane((bid < p.pre_blocks ? bid : bid - p.pre_blocks) * 4 + (int)(threadIdx.x >> 6));
     if (bid < p.pre_blocks) {
         if (item < p.pre_items) prefix_item<D, NSET>(p, item);
     } else if (item < p.suf_items) {
@@ -707,6 +863,11 @@ int launch_decode_multi(const MultiLaunch& a, const char** err) {
     prm.max_q = a.max_q;
     prm.n_tiles = a.n_tiles;
     prm.pre_items = a.Hkv * a.n_tiles * a.n_parts * a.B;   // host-checked to fit
+    // work classes of 256 tokens (more per class for partitions beyond 256k tokens)
+    int qsh = 8;
+    while (((a.part_tokens + (1 << qsh) - 1) >> qsh) > kLptBuckets) ++qsh;
+    prm.lpt_shift = qsh;
+    prm.lpt_buckets = (a.longest_first && a.B <= kLptSeqs) ? (a.part_tokens + (1 << qsh) - 1) >> qsh : 0;
     if (a.B == 0 || a.total_q == 0) return 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(a.stream);
     const hipError_t e = a.D == 64 ? launch_multi_d<64>(prm, a.nset, s)

@@ -37,6 +37,7 @@ _SIGS = {
     "pa_set_partition_tokens": (_i32, [_i32]),
     "pa_set_decode_path": (_i32, [_i32]),
     "pa_set_stream_waves": (_i32, [_i32, _i32]),
+    "pa_set_multi_order": (_i32, [_i32]),
     "pa_decode_shared": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_decode_shared_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -147,6 +148,10 @@ def pa_set_decode_path(path):
 
 def pa_set_stream_waves(waves, min_slice=0):
     _check(_lib.pa_set_stream_waves(int(waves), int(min_slice)))
+
+
+def pa_set_multi_order(longest_first):
+    _check(_lib.pa_set_multi_order(int(longest_first)))
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, workspace=None,

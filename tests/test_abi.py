@@ -152,6 +152,11 @@ def test_decode_path_and_stream_settings():
     for waves, mins in ((-4, 0), (4097, 0), (8, -1)):
         with pytest.raises(pa.PaError):
             pa.pa_set_stream_waves(waves, mins)
+    for bad in (-1, 2):
+        with pytest.raises(pa.PaError):
+            pa.pa_set_multi_order(bad)
+    pa.pa_set_multi_order(0)
+    pa.pa_set_multi_order(1)
     pa.pa_set_decode_path(pa.PA_PATH_STREAM)
     try:
         # the stream decomposition serves bf16 only: forced on fp32 it is refused on the host

@@ -76,6 +76,7 @@ MULTI = [
     ("g1", [100, 250, 64], [7, 250, 1], 4, 4, 128, 16),
     ("d64-g8-bs64", [700, 130, 1], [70, 130, 1], 64, 8, 64, 64),   # one-token prompt
     ("g2-long", [3000, 2500], [40, 1], 16, 8, 128, 32),             # split partitions, G=2
+    ("g5-mixed", [9000, 300, 5000], [600, 300, 40], 40, 8, 128, 16),  # G=5, partitions
 ]
 
 
@@ -209,3 +210,26 @@ def test_stream_and_tile_decompositions_agree(pa):
     finally:
         pa.pa_set_decode_path(pa.PA_PATH_AUTO)
     assert max_err(a, b) <= TOL[W.BF16]
+
+
+@pytest.mark.parametrize("case", MULTI[1:] + [
+    ("chunk-bench", [1024, 2048, 3072, 4096], [1024] * 4, 32, 8, 128, 16),
+    ("long-tile-last", [4096, 4064], [4096, 64], 32, 8, 128, 16),
+], ids=lambda c: c[0])
+def test_longest_first_and_grid_order_give_the_same_bits(pa, case):
+    """The query-tile work is handed out longest first by default; the plain grid order
+    runs the same units, each with the same arithmetic, so every output bit agrees."""
+    name, lens, n_new, Hq, Hkv, D, bs = case
+    wl = W.make_workload(f"mq-order-{name}", len(lens), Hq, Hkv, D, bs, lens, W.BF16, seed=77,
+                         n_new=n_new)
+    note(f"multi order {name}: lens={lens} n={n_new}")
+    outs = []
+    try:
+        for order in (1, 0):
+            pa.pa_set_multi_order(order)
+            (o,), _ = _multi_gpu(pa, wl)
+            outs.append(o)
+    finally:
+        pa.pa_set_multi_order(1)
+    assert np.all(np.isfinite(outs[0]))
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))

@@ -111,3 +111,173 @@ def test_plans_of_the_benchmark_shapes():
     assert plan(4, 1024, 32, 8, 4096) == (4, 64, 4096, 1)
     # a 66-group partition needs two table windows
     assert plan(2, 512, 64, 8, 2112)[2] == 1056
+
+
+# ---------------------------------------------------------------- longest-first order
+# The kernel hands query-tile units (sequence, partition, tile) to the waves in decreasing
+# work: ntok, the partition's tokens that the tile's last query sees, counted in classes of
+# Q tokens; within a class by sequence, partition, then tile from the last. Each block
+# derives the order from the lengths (histogram of classes, scan, then rank -> unit). The
+# arithmetic below repeats the kernel's, integer for integer.
+
+LPT_BUCKETS = 1024
+
+
+def _tiles_from(y, base, n, nt, G, rshift):
+    d = y - base - 1
+    if d < 0:
+        return nt
+    if n <= d:
+        return 0
+    return nt + 1 - ((d * G + (1 << rshift)) >> rshift)
+
+
+def _seqs(lens, n_new, cap, max_q):
+    q_starts = np.concatenate([[0], np.cumsum(n_new)]).astype(int)
+    total_q = int(q_starts[-1])
+    out = []
+    for b in range(len(lens)):
+        L = min(max(int(lens[b]), 0), cap)
+        qs = min(max(int(q_starts[b]), 0), total_q)
+        n = min(max(int(q_starts[b + 1]) - qs, 0), L, max_q, total_q - qs)
+        out.append((L - n, n))
+    return out
+
+
+def lpt_units(lens, n_new, Hq, Hkv, cap):
+    """[(b, part, tile)] in the order the kernel's ranks 0, 1, ... map to."""
+    B, G = len(lens), Hq // Hkv
+    nset, n_tiles, P, n_parts = plan(B, max(n_new), Hq, Hkv, cap)
+    rshift = 4 + {1: 0, 2: 1, 4: 2}[nset]
+    qsh = 8
+    while (P + (1 << qsh) - 1) >> qsh > LPT_BUCKETS:
+        qsh += 1
+    K = (P + (1 << qsh) - 1) >> qsh
+    seq = _seqs(lens, n_new, cap, max(n_new))
+
+    def class_tiles(k, part, base, n, nt):
+        lo = part * P + ((k - 1) << qsh)
+        a = _tiles_from(lo + 1, base, n, nt, G, rshift)
+        c = _tiles_from(lo + (1 << qsh) + 1, base, n, nt, G, rshift) if k < K else 0
+        return a, c
+
+    hist = [0] * K
+    NP = B * n_parts
+    for pr in range(NP):
+        b, part = divmod(pr, n_parts)
+        base, n = seq[b]
+        L = base + n
+        if n <= 0 or part * P >= L:
+            continue
+        nt = (n * G + 16 * nset - 1) >> rshift
+        tf = nt - _tiles_from(part * P + 1, base, n, nt, G, rshift)
+        vf = base + (min((tf + 1) << rshift, n * G) - 1) // G + 1
+        k_lo = (min(vf, (part + 1) * P) - part * P + (1 << qsh) - 1) >> qsh
+        k_hi = (min(L, (part + 1) * P) - part * P + (1 << qsh) - 1) >> qsh
+        for k in range(k_lo, k_hi + 1):
+            a, c = class_tiles(k, part, base, n, nt)
+            if a > c:
+                hist[K - k] += a - c
+    start = np.concatenate([[0], np.cumsum(hist)[:-1]]).astype(int)
+    total = int(start[-1] + hist[-1])
+    units = []
+    for rank in range(total):
+        lo_, hi_ = 0, K - 1
+        while lo_ < hi_:
+            mid = (lo_ + hi_ + 1) >> 1
+            if start[mid] <= rank:
+                lo_ = mid
+            else:
+                hi_ = mid - 1
+        k, j = K - lo_, rank - int(start[lo_])
+        found = None
+        for pr in range(NP):                       # the kernel scans 64 pairs at a time
+            b, part = divmod(pr, n_parts)
+            base, n = seq[b]
+            if n <= 0 or part * P >= base + n:
+                continue
+            nt = (n * G + 16 * nset - 1) >> rshift
+            a, c = class_tiles(k, part, base, n, nt)
+            cnt = max(a - c, 0)
+            if j < cnt:
+                found = (b, part, nt - c - 1 - j)
+                break
+            j -= cnt
+        assert found is not None
+        units.append(found)
+    return units, (nset, n_tiles, P, n_parts, qsh)
+
+
+def _grid_units(lens, n_new, Hq, Hkv, cap):
+    """The units the grid order runs (M > 0 and a partition start at or before the tile's
+    last position), with their ntok."""
+    B, G = len(lens), Hq // Hkv
+    nset, n_tiles, P, n_parts = plan(B, max(n_new), Hq, Hkv, cap)
+    seq = _seqs(lens, n_new, cap, max(n_new))
+    out = {}
+    for b in range(B):
+        base, n = seq[b]
+        for part in range(n_parts):
+            for tile in range(n_tiles):
+                row0 = tile * 16 * nset
+                M = min(16 * nset, n * G - row0)
+                if M <= 0:
+                    continue
+                pos_last = base + (row0 + M - 1) // G
+                if part * P > pos_last:
+                    continue
+                out[(b, part, tile)] = min(pos_last + 1, (part + 1) * P) - part * P
+    return out
+
+
+LPT_CASES = [
+    ([5, 16, 40], [5, 3, 17], 8, 2, 16),
+    ([300, 700], [300, 700], 32, 8, 32),
+    ([1500, 2100], [256, 512], 64, 8, 64),
+    ([40, 1, 333, 90, 17], [0, 1, 33, 90, 4], 16, 4, 128),
+    ([100, 250, 64], [7, 250, 1], 4, 4, 16),
+    ([1024, 2048, 3072, 4096], [1024] * 4, 32, 8, 16),        # the prompt-chunk batch
+    ([4096, 4064], [4096, 64], 32, 8, 16),                     # a long tile behind a prefill
+    ([9000, 300, 5000], [600, 300, 40], 40, 8, 16),             # G = 5
+]
+
+
+@pytest.mark.parametrize("lens, n_new, Hq, Hkv, bs", LPT_CASES)
+def test_longest_first_runs_every_unit_once_in_class_order(lens, n_new, Hq, Hkv, bs):
+    cap = bs * -(-max(lens) // bs)
+    units, (nset, n_tiles, P, n_parts, qsh) = lpt_units(lens, n_new, Hq, Hkv, cap)
+    grid = _grid_units(lens, n_new, Hq, Hkv, cap)
+    assert len(units) == len(set(units)) and set(units) == set(grid)   # a bijection
+    assert len(units) <= len(lens) * n_tiles * n_parts                 # ranks within the grid
+    cls = [-(-grid[u] // (1 << qsh)) for u in units]
+    assert cls == sorted(cls, reverse=True)                            # longest class first
+    for a, c, ka, kc in zip(units, units[1:], cls, cls[1:]):
+        if ka == kc:                                                   # then sequence, partition,
+            assert (a[0], a[1], -a[2]) < (c[0], c[1], -c[2])           # tile from the last
+
+
+def _makespan(works, slots=256, fixed=2.0):
+    import heapq
+    h = [0.0] * slots
+    for w in works:
+        t = heapq.heappop(h)
+        heapq.heappush(h, t + w + fixed)
+    return max(h)
+
+
+def test_longest_first_balances_the_chunk_batch():
+    """The prompt-chunk batch (four 1024-token chunks after 0 .. 3072 cached tokens) on 256
+    four-wave blocks, each unit's 8 KV heads taking two blocks of equal work: in grid order
+    the long chunks' tiles start last and the slowest CU runs about a quarter over the
+    average; longest first it runs at the average."""
+    lens, n_new, Hq, Hkv, cap = [1024, 2048, 3072, 4096], [1024] * 4, 32, 8, 4096
+    grid = _grid_units(lens, n_new, Hq, Hkv, cap)
+    units, (nset, n_tiles, P, n_parts, _) = lpt_units(lens, n_new, Hq, Hkv, cap)
+    steps = lambda u: -(-grid[u] // 32)                     # 32 tokens per softmax step
+    natural = [(b, part, n_tiles - 1 - t) for b in range(4) for part in range(n_parts)
+               for t in range(n_tiles)]
+    natural = [u for u in natural if u in grid]
+    per_block = lambda order: [steps(u) for u in order for _ in range(Hkv // 4)]
+    ideal = sum(per_block(units)) / 256 + 2.0
+    assert _makespan(per_block(natural)) > 1.2 * ideal
+    assert _makespan(per_block(units)) < 1.02 * ideal
