@@ -400,18 +400,25 @@ __device__ __forceinline__ void multi_item(const Params& p, int g, int b, int pa
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // scores of one group for every set: y[s][o + i] for tokens r + 4i of the group
+    // scores of one group for every set: y[s][o + i] for tokens r + 4i of the group. The
+    // sets' accumulations are interleaved (head-dim chunk outer, set inner), so NSET
+    // independent products are in flight instead of one dependent chain.
     auto qk = [&](const Item& kit, float (&y)[NSET][8], int o) {
+        f32x4_t sc[NSET];
+#pragma unroll
+        for (int s = 0; s < NSET; ++s) sc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+#pragma unroll
+            for (int s = 0; s < NSET; ++s)
+                sc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, kit.q[k]),
+                    __builtin_bit_cast(bf16x8_t, qf[s][k]), sc[s], 0, 0, 0);
+        }
 #pragma unroll
         for (int s = 0; s < NSET; ++s) {
-            f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int k = 0; k < NQ; ++k)
-                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, kit.q[k]),
-                    __builtin_bit_cast(bf16x8_t, qf[s][k]), sc, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[s][o + i] = sc[i] * cl2;
+            for (int i = 0; i < 4; ++i) y[s][o + i] = sc[s][i] * cl2;
         }
     };
     // rows past `valid` of a V item may hold anything: their probabilities are 0, their
@@ -451,10 +458,9 @@ __device__ __forceinline__ void multi_item(const Params& p, int g, int b, int pa
         __builtin_amdgcn_sched_barrier(0);
         // the causal edge, the partition's end or a missing second group fall in this pair
         const bool edge = tg + 31 > pos_first || !live1;
-        uint32_t pw[NSET][4];
+        if (edge) {
 #pragma unroll
-        for (int s = 0; s < NSET; ++s) {
-            if (edge) {
+            for (int s = 0; s < NSET; ++s) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int tok = tg + (i >> 2) * 16 + r + 4 * (i & 3);
@@ -462,28 +468,47 @@ __device__ __forceinline__ void multi_item(const Params& p, int g, int b, int pa
                     y[s][i] = ok ? y[s][i] : -INFINITY;
                 }
             }
-            float mx = y[s][0];
+        }
+        // m_run is each column's reference, not always its maximum: it moves (and the
+        // accumulators are rescaled) only when some column's maximum passes its reference
+        // by more than PA_LAZY_RESCALE (log2 units), so the probabilities stay below
+        // 2^PA_LAZY_RESCALE. Softmax does not depend on the reference, and a column that
+        // has seen no token yet moves at its first token. A column with no token keeps
+        // m = -inf and 0 as the exponent reference, so its factors are 0.
+        // A column's maximum passes its reference exactly when one of the four lanes that
+        // hold the column has a score past it, so the common step tests each lane's own
+        // maximum (one ballot for all sets, no cross-lane reduction) and the column maxima
+        // are formed only when some set moves; the decision is still per set.
+        float mx[NSET];
+        bool move = false;
 #pragma unroll
-            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, y[s][i]);
-            const float m_new = fmaxf(m_run[s], rows_max(mx));
-            // m_run is each column's reference, not always its maximum: it moves (and the
-            // accumulators are rescaled) only when some column's maximum passes its
-            // reference by more than PA_LAZY_RESCALE (log2 units), so the probabilities
-            // stay below 2^PA_LAZY_RESCALE. Softmax does not depend on the reference, and a
-            // column that has seen no token yet moves at its first token. A column with no
-            // token keeps m = -inf and 0 as the exponent reference, so its factors are 0.
-            if (__ballot(m_new > m_run[s] + (float)PA_LAZY_RESCALE) != 0) {
-                const float m_to = m_new == -INFINITY ? 0.f : m_new;
-                const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_to);   // per column
-                m_run[s] = m_new;
+        for (int s = 0; s < NSET; ++s) {
+            mx[s] = y[s][0];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float ai = col_bcast(alpha, i);
+            for (int i = 1; i < 8; ++i) mx[s] = __builtin_elementwise_maximum(mx[s], y[s][i]);
+            move = move || mx[s] > m_run[s] + (float)PA_LAZY_RESCALE;
+        }
+        if (__ballot(move) != 0) {
 #pragma unroll
-                    for (int e = 0; e < EV; ++e) acc[s][e][i] *= ai;
-                    lsum[s][i] *= ai;
+            for (int s = 0; s < NSET; ++s) {
+                const float m_new = fmaxf(m_run[s], rows_max(mx[s]));
+                if (__ballot(m_new > m_run[s] + (float)PA_LAZY_RESCALE) != 0) {
+                    const float m_to = m_new == -INFINITY ? 0.f : m_new;
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_to);   // per column
+                    m_run[s] = m_new;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float ai = col_bcast(alpha, i);
+#pragma unroll
+                        for (int e = 0; e < EV; ++e) acc[s][e][i] *= ai;
+                        lsum[s][i] *= ai;
+                    }
                 }
             }
+        }
+        uint32_t pw[NSET][4];
+#pragma unroll
+        for (int s = 0; s < NSET; ++s) {
             const float m_ref = m_run[s] == -INFINITY ? 0.f : m_run[s];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
@@ -500,28 +525,39 @@ __device__ __forceinline__ void multi_item(const Params& p, int g, int b, int pa
             zero_rows(v0, ntok - 16 * t);
             zero_rows(v1, live1 ? ntok - 16 * (t + 1) : 0);
         }
+        // every V operand first (its own registers), so the 8 NSET products that follow
+        // issue back to back instead of waiting to overwrite the operand the previous
+        // products still read
+        u32x4_t bv[WV / 4][2];
 #pragma unroll
         for (int w = 0; w < WV / 4; ++w) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const uint32_t sel = h ? 0x07060302u : 0x05040100u;
-                const u32x4_t bv = {__builtin_amdgcn_perm(vword(v0, 1, w), vword(v0, 0, w), sel),
-                                    __builtin_amdgcn_perm(vword(v0, 3, w), vword(v0, 2, w), sel),
-                                    __builtin_amdgcn_perm(vword(v1, 1, w), vword(v1, 0, w), sel),
-                                    __builtin_amdgcn_perm(vword(v1, 3, w), vword(v1, 2, w), sel)};
-#pragma unroll
-                for (int s = 0; s < NSET; ++s) {
-                    const u32x4_t av = {pw[s][0], pw[s][1], pw[s][2], pw[s][3]};
-                    acc[s][2 * w + h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv),
-                        acc[s][2 * w + h], 0, 0, 0);
-                }
+                bv[w][h] = u32x4_t{__builtin_amdgcn_perm(vword(v0, 1, w), vword(v0, 0, w), sel),
+                                   __builtin_amdgcn_perm(vword(v0, 3, w), vword(v0, 2, w), sel),
+                                   __builtin_amdgcn_perm(vword(v1, 1, w), vword(v1, 0, w), sel),
+                                   __builtin_amdgcn_perm(vword(v1, 3, w), vword(v1, 2, w), sel)};
             }
         }
         __builtin_amdgcn_sched_barrier(0);
         issue_v(t + 2, v0);
         __builtin_amdgcn_sched_barrier(0);
         issue_v(t + 3, v1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int w = 0; w < WV / 4; ++w) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int s = 0; s < NSET; ++s) {
+                    const u32x4_t av = {pw[s][0], pw[s][1], pw[s][2], pw[s][3]};
+                    acc[s][2 * w + h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv[w][h]),
+                        acc[s][2 * w + h], 0, 0, 0);
+                }
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
 
