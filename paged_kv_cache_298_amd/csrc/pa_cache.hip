@@ -112,9 +112,13 @@ __global__ __launch_bounds__(256) void read_tiles_kernel(const char* __restrict_
             u32x4_t r[TB][2 * NCH];
 #pragma unroll
             for (int t = 0; t < TB; ++t) {
+                // a batch past the slice's last tile reads the first tile of the caches
+                // instead (not XORed; one tile every wave reads stays in cache)
                 const int tt = min(u0 + t, cnt - 1);
-                const int64_t off = (int64_t)(((uint64_t)__builtin_amdgcn_readlane(my_hi, tt) << 32) |
-                                              (uint64_t)__builtin_amdgcn_readlane(my_lo, tt));
+                const int64_t off = u0 + t < cnt
+                    ? (int64_t)(((uint64_t)__builtin_amdgcn_readlane(my_hi, tt) << 32) |
+                                (uint64_t)__builtin_amdgcn_readlane(my_lo, tt))
+                    : 0;
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {
                     r[t][i] = __builtin_nontemporal_load(

@@ -530,9 +530,13 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
     struct Item {
         u32x4_t q[NQ];
     };
+    // Groups past the slice (the ring runs DEPTH / 2 groups ahead of the consumer) are
+    // parked on the first tile of the caches: the data are never used, and one small tile
+    // that every wave reads stays in cache, where a re-read of the slice's last group would
+    // fetch it from HBM again (the loads are non-temporal).
     auto tile_off = [&](int gq) -> uint64_t {
         int s = s0 + gq;
-        s = s < s1 ? s : s1 - 1;
+        if (s >= s1) return 0;
         if (s - sw >= 64) {
             sw += 64;
             window(sw);
@@ -544,7 +548,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
     // SPLIT: the second block's tile of the same group (the window is already in place)
     auto tile_off1 = [&](int gq) -> uint64_t {
         int s = s0 + gq;
-        s = s < s1 ? s : s1 - 1;
+        if (s >= s1) return 0;
         const int idx = s - sw;
         return ((uint64_t)__builtin_amdgcn_readlane(w_hi1, idx) << 32) |
                (uint64_t)__builtin_amdgcn_readlane(w_lo1, idx);

@@ -168,6 +168,15 @@ def test_loose_max_q_bound_and_empty_chunks(pa, oracle):
     assert max_err(out.cpu().numpy(), ref) <= TOL[W.BF16]
 
 
+def test_more_sequences_than_the_longest_first_order_holds(pa, oracle):
+    """2100 sequences (the longest-first order handles up to 2048; beyond that the waves
+    take the query tiles in grid order): every row against the oracle."""
+    rng = np.random.default_rng(2100)
+    lens = rng.integers(6, 41, size=2100)
+    wl = W.make_workload("mq-many", 2100, 8, 2, 64, 16, lens, W.BF16, seed=2100, n_new=[6] * 2100)
+    _parity(pa, oracle, wl, "2100 sequences (grid order)")
+
+
 # ------------------------------------------------ the stream decomposition (<= 16 columns)
 
 STREAM = [
