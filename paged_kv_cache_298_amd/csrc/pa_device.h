@@ -486,13 +486,17 @@ __device__ __forceinline__ void bf16_item(const Params& p, int id) {
     };
     // load stream item t of chunk ch (t < kChunk: K of group t, else V of group t - kChunk);
     // groups past the partition are clamped to its last group (a re-read that hits in cache)
+    // slots past the stream's last group (the last chunk's tail) read the first tile of
+    // the head instead: the data are never used, and that tile stays in cache, where a
+    // re-read of the last group would fetch it from HBM again (non-temporal loads)
     auto issue = [&](int ch, int t, Item& dst) {
         const bool is_v = t >= kChunk;
         int gi = ch * kChunk + (is_v ? t - kChunk : t);
+        const bool past = gi > last;
         gi = gi < last ? gi : last;
         const int ph = __builtin_amdgcn_readlane(tblv, gi);
         const int tok = t0 + (wid + gi * W) * 16;
-        const int64_t off = (int64_t)ph * blk_bytes + (int64_t)(tok & bs_mask) * ROW;
+        const int64_t off = past ? 0 : (int64_t)ph * blk_bytes + (int64_t)(tok & bs_mask) * ROW;
         if (!is_v) {
             const char* kb = kbase + off;
 #pragma unroll

@@ -91,8 +91,10 @@ __device__ __forceinline__ void prefix_item(const Params& p, int id) {
     struct Item {
         u32x4_t q[NQ];
     };
+    // groups past the partition (the ring runs two ahead) read the head's first tile
+    // instead: never used, and it stays in cache (the loads are non-temporal)
     auto goff = [&](int gq) -> int64_t {
-        gq = gq < last ? gq : last;
+        if (gq > last) return 0;
         const int ph = __builtin_amdgcn_readlane(tblv, gq);
         return (int64_t)ph * blk_bytes + (int64_t)((t0 + gq * 16) & bs_mask) * ROW;
     };
