@@ -281,3 +281,28 @@ def test_longest_first_balances_the_chunk_batch():
     ideal = sum(per_block(units)) / 256 + 2.0
     assert _makespan(per_block(natural)) > 1.2 * ideal
     assert _makespan(per_block(units)) < 1.02 * ideal
+
+
+def test_longest_first_on_random_batches():
+    """Random batches (lengths, chunk sizes, head ratios, block sizes, partitions): the
+    longest-first ranks still cover every unit of the grid order exactly once, in class
+    order, within the grid's rank range."""
+    rng = np.random.default_rng(7301)
+    for _ in range(40):
+        B = int(rng.integers(1, 9))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        bs = int(rng.choice([16, 32, 64, 128]))
+        lens = [int(x) for x in rng.integers(0, 3000, size=B)]
+        n_new = [int(rng.integers(0, L + 1)) if L > 0 else 0 for L in lens]
+        if max(n_new) * G <= 16:           # one score tile per row: the stream path, not tiles
+            n_new[0] = min(lens[0], 17) if lens[0] else 0
+            if max(n_new) * G <= 16:
+                continue
+        cap = bs * max(1, -(-max(max(lens), 1) // bs))
+        units, (nset, n_tiles, P, n_parts, qsh) = lpt_units(lens, n_new, G * Hkv, Hkv, cap)
+        grid = _grid_units(lens, n_new, G * Hkv, Hkv, cap)
+        assert len(units) == len(set(units)) and set(units) == set(grid)
+        assert len(units) <= B * n_tiles * n_parts
+        cls = [-(-grid[u] // (1 << qsh)) for u in units]
+        assert cls == sorted(cls, reverse=True)
