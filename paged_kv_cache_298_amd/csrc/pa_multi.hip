@@ -29,7 +29,11 @@ __device__ __forceinline__ void prefix_item(const Params& p, int id) {
     constexpr int NQ = D / 32;
     constexpr int WV = D / 8;
     constexpr int EV = D / 16;
-    constexpr int DEPTH = 4;             // ring items: K and V of two groups
+    // ring items: K and V of one group. The suffix items that run beside these waves are
+    // short and bound by chains of dependent reads; a shallower ring here leaves them more
+    // of the memory system (2 groups ahead measured 59.2 us on the shared-prefix batch,
+    // 1 group 58.3, 4 groups 62.8)
+    constexpr int DEPTH = 2;
     constexpr int U = DEPTH / 2;
     static_assert(D == 64 || D == 128, "head size");
 
