@@ -23,12 +23,6 @@
 #ifndef PA_BF16_QLDS
 #define PA_BF16_QLDS 0
 #endif
-#ifndef PA_SHARED_DEPTH
-#define PA_SHARED_DEPTH 4
-#endif
-#ifndef PA_SHARED_CHUNK
-#define PA_SHARED_CHUNK 4
-#endif
 #ifndef PA_BF16_WAVES
 #define PA_BF16_WAVES 4
 #endif
@@ -221,8 +215,8 @@ __device__ __forceinline__ u32x4_t kv_load16(const u32x4_t* ptr) {
 #endif
 }
 
-// Non-temporal K/V loads of the bf16 partition item (partition decode, shared-prefix
-// suffixes) and of the shared-prefix tiles, each read once per call.
+// Non-temporal K/V loads of the bf16 partition item (partition decode) and of the
+// shared-prefix row items, each read once per call.
 #ifndef PA_ITEM_NT
 #define PA_ITEM_NT 1
 #endif
@@ -408,15 +402,7 @@ __device__ __forceinline__ void bf16_item(const Params& p, int id) {
     int L = p.lens[b];
     L = L < 0 ? 0 : (L > cap ? cap : L);
     const int hq0 = g * G;
-    // shared-prefix mode: this kernel covers only the tokens after the shared prefix and
-    // always leaves partial records (slots after the prefix partitions)
-    const bool shared = p.groups != nullptr;
-    int start = 0, slot0 = 0;
-    if (shared) {
-        start = min(group_shared(p, b), L);
-        slot0 = (start + p.pre_tokens - 1) / p.pre_tokens;
-    }
-    const int t0 = start + part * p.part_tokens;
+    const int t0 = part * p.part_tokens;
     // Wave wid takes the partition's 16-token groups wid, wid + W, wid + 2W, ... (its
     // "local" groups 0, 1, 2, ...). The block-table entries of those groups are fetched
     // before the sequence length is known (they do not depend on it): lane i holds the
@@ -431,7 +417,7 @@ __device__ __forceinline__ void bf16_item(const Params& p, int id) {
         tblv = e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);
     }
     if (t0 >= L) {
-        if (part == 0 && !shared) {   // empty sequence: a zero row per head
+        if (part == 0) {   // empty sequence: a zero row per head
             for (int i = threadIdx.x; i < G * D; i += 64 * W)
                 p.out[((int64_t)b * p.Hq + hq0) * D + i] = 0.f;
         }
@@ -445,8 +431,8 @@ __device__ __forceinline__ void bf16_item(const Params& p, int id) {
     const int last = ngroups - 1;
     const int ntok = ngroups > 0 ? last * 16 + min(16, ntok_part - (wid + last * W) * 16) : 0;
     const int nchunks = (ngroups + kChunk - 1) / kChunk;
-    const int nparts_b = shared ? 0 : (L + p.part_tokens - 1) / p.part_tokens;   // 0: records
-    const int slot = slot0 + part;
+    const int nparts_b = (L + p.part_tokens - 1) / p.part_tokens;
+    const int slot = part;
 
     const int r = lane >> 4;     // row group
     const int c = lane & 15;     // column

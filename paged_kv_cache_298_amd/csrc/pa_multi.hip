@@ -11,50 +11,43 @@
 // score tiles, so one K/V tile read serves all of them.
 #include "pa_device.h"
 
+// ring items of a suffix item (K and V of PA_SUFFIX_DEPTH / 2 groups in flight); one
+// group ahead measured best on the shared-prefix batch (57.3 us; two 57.7, three 58.2)
+#ifndef PA_SUFFIX_DEPTH
+#define PA_SUFFIX_DEPTH 2
+#endif
+
 namespace {
 
 // Shared prefix (parallel sampling, shared prompts): the leading tokens a group of
-// sequences shares are read once for all of them. One wavefront per (group, KV head,
-// partition of pre_tokens tokens); the M = members x G query rows of the group are the
-// columns of the score tiles (set s holds rows 16 s .. 16 s + 15, zero past M), so each K
-// and V tile feeds every member. Scores: v_mfma_f32_16x16x32_bf16, lane (r, c) then holds
-// tokens r + 4i of query row 16 s + c; online softmax per column; PV:
+// sequences shares are read once for all of them, and each member's own tokens once for
+// that member. Both kinds of work are a row item: the rows of `members` consecutive
+// sequences from `first` (M = members x G query rows, the columns of the score tiles; set
+// s holds rows 16 s .. 16 s + 15, zero past M) over tokens [t0, t0 + ntok), read through
+// the block table of `first` (for a prefix item every member's table holds the same blocks
+// there), so each K and V tile feeds every member. Scores: v_mfma_f32_16x16x32_bf16, lane
+// (r, c) then holds tokens r + 4i of query row 16 s + c; online softmax per column; PV:
 // v_mfma_f32_16x16x16_bf16 with those probabilities (rounded to bf16) as A, leaving lane
 // (r, c) with query rows 16 s + 4 r + i of output columns c * EV .. c * EV + EV - 1. Every
-// (member, head) gets a partial record in slot `part`; the partition merge combines them
-// with the members' own tokens.
-template <int D, int NSET>
-__device__ __forceinline__ void prefix_item(const Params& p, int id) {
+// (member, head) gets a partial record in slot `slot` (slot < 0: the row's only partition,
+// written normalized to `out`); the partition merge combines the prefix and own-token
+// records. DEPTH ring items: K and V of DEPTH / 2 groups ahead of the
+// consumer, K and V of a group issued together.
+template <int D, int NSET, int DEPTH>
+__device__ __forceinline__ void row_item(const Params& p, int g, int first, int members, int t0,
+                                         int ntok, int slot) {
     constexpr int ROW = D * 2;
     constexpr int NQ = D / 32;
     constexpr int WV = D / 8;
     constexpr int EV = D / 16;
-    // ring items: K and V of one group. The suffix items that run beside these waves are
-    // short and bound by chains of dependent reads; a shallower ring here leaves them more
-    // of the memory system (2 groups ahead measured 59.2 us on the shared-prefix batch,
-    // 1 group 58.3, 4 groups 62.8)
-    constexpr int DEPTH = 2;
     constexpr int U = DEPTH / 2;
     static_assert(D == 64 || D == 128, "head size");
+    static_assert(DEPTH >= 2 && DEPTH % 2 == 0, "ring holds whole groups (K and V)");
 
     const int lane = threadIdx.x & 63;
-    const int g = id % p.Hkv;
-    const int rest = id / p.Hkv;
-    const int gi_ = rest % p.n_groups;
-    const int part = rest / p.n_groups;
-    const int first = p.groups[3 * gi_];
-    int members = p.groups[3 * gi_ + 1];
-    members = members > p.max_members ? p.max_members : members;
-    members = members > p.B - first ? p.B - first : members;   // stay inside the batch
-    const int cap = p.max_blocks * p.bs;
-    int shared_tok = p.groups[3 * gi_ + 2];
-    shared_tok = (shared_tok > p.max_shared ? p.max_shared : shared_tok) & ~15;   // whole groups
-    shared_tok = shared_tok < 0 ? 0 : (shared_tok > cap ? cap : shared_tok);
     const int G = p.Hq / p.Hkv;
     const int M = members * G;           // query rows (host checks M <= 16 * NSET)
-    const int t0 = part * p.pre_tokens;
-    if (first < 0 || first >= p.B || t0 >= shared_tok || members <= 0) return;
-    const int ntok = min(p.pre_tokens, shared_tok - t0);
+    const int part = slot;
     const int ng = (ntok + 15) >> 4;
     const int last = ng - 1;
 
@@ -249,15 +242,79 @@ __device__ __forceinline__ void prefix_item(const Params& p, int id) {
             if (qr < M) {
                 const int mb = qr / G, hh = qr - mb * G;
                 const int64_t row = (int64_t)(first + mb) * p.Hq + g * G + hh;
-                float* dst = p.ws_o + (row * p.n_parts + part) * D + c * EV;
+                if (slot < 0) {        // the row's only partition: the normalized output
+                    const float inv = 1.0f / lr;
+                    float* dst = p.out + row * D + c * EV;
 #pragma unroll
-                for (int e = 0; e < EV; e += 4)
-                    *reinterpret_cast<float4*>(dst + e) =
-                        make_float4(acc[s][e][i], acc[s][e + 1][i], acc[s][e + 2][i], acc[s][e + 3][i]);
-                if (c == 0) p.ws_ml[row * p.n_parts + part] = make_float2(mr, lr);
+                    for (int e = 0; e < EV; e += 4)
+                        *reinterpret_cast<float4*>(dst + e) =
+                            make_float4(acc[s][e][i] * inv, acc[s][e + 1][i] * inv,
+                                        acc[s][e + 2][i] * inv, acc[s][e + 3][i] * inv);
+                } else {
+                    float* dst = p.ws_o + (row * p.n_parts + part) * D + c * EV;
+#pragma unroll
+                    for (int e = 0; e < EV; e += 4)
+                        *reinterpret_cast<float4*>(dst + e) =
+                            make_float4(acc[s][e][i], acc[s][e + 1][i], acc[s][e + 2][i], acc[s][e + 3][i]);
+                    if (c == 0) p.ws_ml[row * p.n_parts + part] = make_float2(mr, lr);
+                }
             }
         }
     }
+}
+
+// A prefix item: (group, KV head, partition of pre_tokens shared tokens). Its ring runs
+// one group ahead: the suffix items that run beside these waves are short and bound by
+// chains of dependent reads, and a shallower ring here leaves them more of the memory
+// system (2 groups ahead measured 59.2 us on the shared-prefix batch, 1 group 58.3,
+// 4 groups 62.8).
+template <int D, int NSET>
+__device__ __forceinline__ void prefix_item(const Params& p, int id) {
+    const int g = id % p.Hkv;
+    const int rest = id / p.Hkv;
+    const int gi_ = rest % p.n_groups;
+    const int part = rest / p.n_groups;
+    const int first = p.groups[3 * gi_];
+    int members = p.groups[3 * gi_ + 1];
+    members = members > p.max_members ? p.max_members : members;
+    members = members > p.B - first ? p.B - first : members;   // stay inside the batch
+    const int cap = p.max_blocks * p.bs;
+    int shared_tok = p.groups[3 * gi_ + 2];
+    shared_tok = (shared_tok > p.max_shared ? p.max_shared : shared_tok) & ~15;   // whole groups
+    shared_tok = shared_tok < 0 ? 0 : (shared_tok > cap ? cap : shared_tok);
+    const int t0 = part * p.pre_tokens;
+    if (first < 0 || first >= p.B || t0 >= shared_tok || members <= 0) return;
+    row_item<D, NSET, 2>(p, g, first, members, t0, min(p.pre_tokens, shared_tok - t0), part);
+}
+
+// A suffix item: (sequence, KV head, partition of part_tokens of the sequence's own
+// tokens, those after its group's shared prefix). One member, G query rows in one column
+// set; K and V of a group are loaded together, so a short row costs few dependent round
+// trips. Records go to the slots after the sequence's prefix
+// partitions; a partition past the sequence's end leaves nothing.
+// With no groups at all the launch is a plain partitioned decode: a row with one partition
+// is written normalized, an empty row as zeros, and only longer rows leave records.
+template <int D>
+__device__ __forceinline__ void suffix_item(const Params& p, int id) {
+    int g, b, part;
+    work_item(p, id, g, b, part);
+    const int cap = p.max_blocks * p.bs;
+    int L = p.lens[b];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    const bool plain = p.groups == nullptr;
+    const int start = plain ? 0 : min(group_shared(p, b), L);
+    const int slot0 = (start + p.pre_tokens - 1) / p.pre_tokens;
+    const int t0 = start + part * p.part_tokens;
+    if (t0 >= L) {
+        if (plain && part == 0) {   // empty sequence: a zero row per head
+            const int G = p.Hq / p.Hkv;
+            for (int i = (int)(threadIdx.x & 63); i < G * D; i += 64)
+                p.out[((int64_t)b * p.Hq + g * G) * D + i] = 0.f;
+        }
+        return;
+    }
+    const int slot = plain && L <= p.part_tokens ? -1 : slot0 + part;
+    row_item<D, 1, PA_SUFFIX_DEPTH>(p, g, b, 1, t0, min(p.part_tokens, L - t0), slot);
 }
 
 // Multi-query attention with a causal mask (prefill, a chunk of a long prompt, draft
@@ -789,7 +846,7 @@ __global__ __launch_bounds__(256) void decode_shared_kernel(Params p) {
     if (bid < p.pre_blocks) {
         if (item < p.pre_items) prefix_item<D, NSET>(p, item);
     } else if (item < p.suf_items) {
-        bf16_item<D, G, PA_SHARED_DEPTH, PA_SHARED_CHUNK, false, 1>(p, item);
+        suffix_item<D>(p, item);
     }
 }
 
