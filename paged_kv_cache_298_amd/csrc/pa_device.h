@@ -759,16 +759,21 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
     const float* wo = p.ws_o + row * p.n_parts * D;
     float2 mlv[kB];
     float4 ov[kB];
-    auto load_batch = [&](int k0) {
+    auto load_batch = [&](int k0, int lim) {
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
             int i = pg + NPG * (k0 + u);
-            i = i < p.n_parts ? i : 0;
+            i = i < lim ? i : 0;
             mlv[u] = ml[i];
             ov[u] = reinterpret_cast<const float4*>(wo + (int64_t)i * D)[c4];
         }
     };
-    load_batch(0);
+    // The first batch is loaded before the count is known. In shared-prefix mode it takes
+    // the slots of a full prefix and one own partition (the other slots are there for the
+    // table's capacity and mostly unused); a row with more records loads the rest below.
+    const int spec = p.groups != nullptr
+        ? min(p.n_parts, (p.max_shared + p.pre_tokens - 1) / p.pre_tokens + 1) : p.n_parts;
+    load_batch(0, spec);
 
     const int cap = p.max_blocks * p.bs;
     int np;
@@ -807,10 +812,21 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(Params p) {
         }
     }
 
+    if (np > spec) {
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int i = pg + NPG * u;
+            if (i >= spec && i < np) {
+                mlv[u] = ml[i];
+                ov[u] = reinterpret_cast<const float4*>(wo + (int64_t)i * D)[c4];
+            }
+        }
+    }
+
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float den = 0.f, m = -INFINITY;
     for (int k0 = 0; pg + NPG * k0 < np; k0 += kB) {
-        if (k0 != 0) load_batch(k0);
+        if (k0 != 0) load_batch(k0, p.n_parts);
         float mn = m;
 #pragma unroll
         for (int u = 0; u < kB; ++u)
