@@ -116,8 +116,8 @@ __global__ __launch_bounds__(256) void read_tiles_kernel(const char* __restrict_
                 // instead (not XORed; one tile every wave reads stays in cache)
                 const int tt = min(u0 + t, cnt - 1);
                 const int64_t off = u0 + t < cnt
-                    ? (int64_t)(((uint64_t)__builtin_amdgcn_readlane(my_hi, tt) << 32) |
-                                (uint64_t)__builtin_amdgcn_readlane(my_lo, tt))
+                    ? (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(my_hi, tt) << 32) |
+                                (uint64_t)(uint32_t)__builtin_amdgcn_readlane(my_lo, tt))
                     : 0;
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {

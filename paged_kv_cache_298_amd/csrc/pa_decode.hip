@@ -542,16 +542,18 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(Params p) {
             window(sw);
         }
         const int idx = s - sw;
-        return ((uint64_t)__builtin_amdgcn_readlane(w_hi, idx) << 32) |
-               (uint64_t)__builtin_amdgcn_readlane(w_lo, idx);
+        // readlane returns int: through uint32_t, so that a low word with bit 31 set is not
+        // sign-extended into the high word (tiles past 2 GiB of a cache)
+        return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(w_hi, idx) << 32) |
+               (uint64_t)(uint32_t)__builtin_amdgcn_readlane(w_lo, idx);
     };
     // SPLIT: the second block's tile of the same group (the window is already in place)
     auto tile_off1 = [&](int gq) -> uint64_t {
         int s = s0 + gq;
         if (s >= s1) return 0;
         const int idx = s - sw;
-        return ((uint64_t)__builtin_amdgcn_readlane(w_hi1, idx) << 32) |
-               (uint64_t)__builtin_amdgcn_readlane(w_lo1, idx);
+        return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(w_hi1, idx) << 32) |
+               (uint64_t)(uint32_t)__builtin_amdgcn_readlane(w_lo1, idx);
     };
     auto issue_k = [&](int gq, Item& dst) {
         const uint64_t off = tile_off(gq);
