@@ -118,6 +118,19 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _workspace(need, like, stream):
+    """A workspace the library may fill as it likes (no zero fill, which would race with a
+    launch on another stream), kept from reuse by torch's allocator until the work queued on
+    `stream` has finished with it."""
+    ws = torch.empty(need, dtype=torch.uint8, device=like.device)
+    if stream is not None:
+        s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(
+            int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream), device=like.device)
+        if s != torch.cuda.current_stream(like.device):
+            ws.record_stream(s)
+    return ws
+
+
 def _stream(t, stream):
     if stream is not None:
         return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
@@ -165,7 +178,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, workspace
     max_blocks = block_tables.shape[1]
     need = pa_decode_workspace_bytes(B, Hq, Hkv, D, bs, max_blocks, _kv_dtype(k_cache))
     if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q, stream)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                           _ptr(seq_lens), B, Hq, Hkv, D, bs, nb, max_blocks, float(scale),
@@ -184,7 +197,7 @@ def pa_decode_append(out, q, k_cache, v_cache, key, value, slot_mapping, block_t
     max_blocks = block_tables.shape[1]
     need = pa_decode_workspace_bytes(B, Hq, Hkv, D, bs, max_blocks, _kv_dtype(k_cache))
     if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q, stream)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.pa_decode_append(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value),
                                  _ptr(slot_mapping), _ptr(block_tables), _ptr(seq_lens), B, Hq, Hkv, D, bs,
@@ -219,7 +232,7 @@ def pa_decode_shared(out, q, k_cache, v_cache, block_tables, seq_lens, groups, m
     n_groups = 0 if groups is None else groups.shape[0]
     need = pa_decode_shared_workspace_bytes(B, Hq, D, bs, max_blocks, max_shared_tokens)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q, stream)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.pa_decode_shared(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                  _ptr(block_tables), _ptr(seq_lens),
@@ -246,7 +259,7 @@ def pa_decode_multi(out, q, k_cache, v_cache, block_tables, seq_lens, q_starts, 
     max_blocks = block_tables.shape[1]
     need = pa_decode_multi_workspace_bytes(B, total_q, max_q, Hq, Hkv, D, bs, max_blocks)
     if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q, stream)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.pa_decode_multi(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                 _ptr(block_tables), _ptr(seq_lens), _ptr(q_starts), B, total_q,

@@ -382,6 +382,32 @@ def test_repeated_calls_are_bitwise_equal(pa):
     assert np.array_equal(a, dw.out.cpu().numpy())
 
 
+@pytest.mark.parametrize("path", ["stream", "partition"])
+def test_side_stream_with_library_workspace(pa, path):
+    """pa_decode on a stream other than the current one, with the workspace left to the
+    binding (uninitialised memory, held from reuse until that stream's work is done), while
+    the current stream allocates and fills memory of the same size meanwhile: the bits of
+    the call on the current stream."""
+    wl = W.config(2)
+    dw = DevWorkload(wl)
+    mode = pa.PA_PATH_STREAM if path == "stream" else pa.PA_PATH_PARTITION
+    with _path(pa, mode):
+        note(f"side stream ({path}): reference on the current stream")
+        ref = gpu_step(pa, dw).copy()
+        need = pa.pa_decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.block_size,
+                                            wl.max_blocks, pa.PA_BF16)
+        side = torch.cuda.Stream()
+        out = torch.empty_like(dw.out)
+        side.wait_stream(torch.cuda.current_stream())
+        note(f"side stream ({path}): 3 calls, workspace from the binding")
+        for _ in range(3):
+            pa.pa_decode(out, dw.q, dw.k, dw.v, dw.bt, dw.sl, wl.scale, stream=side)
+            junk = torch.full((need,), 0x7f, dtype=torch.uint8, device=DEV)   # current stream
+            del junk
+        torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
 @pytest.mark.parametrize("P", [64, 128, 512, 1024])
 def test_partition_length_changes_only_rounding(pa, oracle, P):
     wl = W.make_workload("split", 4, 32, 8, 128, 64, [100, 1023, 1025, 4000], W.BF16, seed=P,
