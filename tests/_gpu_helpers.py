@@ -89,3 +89,23 @@ def max_err(got, ref):
     got = np.asarray(got, dtype=np.float64)
     assert np.isfinite(got).all(), "non-finite GPU output"
     return float(np.max(np.abs(got - ref))) if got.size else 0.0
+
+
+def scale_k_by_position(wl, factor_of_pos):
+    """Multiply each token's K row (all KV heads) by factor_of_pos(b, pos, L), in the cache
+    and in the new-token rows alike, rounding back to the cache's element type."""
+    bs = wl.block_size
+    qs = wl.q_starts if wl.q_starts is not None else np.arange(wl.B + 1, dtype=np.int32)
+    n_new = np.diff(qs)
+    to32 = W.bf16_to_f32 if wl.dtype == W.BF16 else (lambda a: a)
+    back = W.bf16_from_f32 if wl.dtype == W.BF16 else (lambda a: a.astype(np.float32))
+    for b in range(wl.B):
+        L, n = int(wl.seq_lens[b]), int(n_new[b])
+        for pos in range(L):
+            f = np.float32(factor_of_pos(b, pos, L))
+            if pos >= L - n:
+                i = int(qs[b]) + pos - (L - n)
+                wl.new_key[i] = back(to32(wl.new_key[i]) * f)
+            else:
+                blk = wl.block_tables[b, pos // bs]
+                wl.k_cache[blk, :, pos % bs] = back(to32(wl.k_cache[blk, :, pos % bs]) * f)

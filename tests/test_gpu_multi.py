@@ -10,7 +10,8 @@ import pytest
 import torch
 
 from paged_kv_cache_298_amd import workloads as W
-from tests._gpu_helpers import DEV, TOL, check_inputs, max_err, note, to_dev
+from tests._gpu_helpers import (DEV, TOL, check_inputs, max_err, note, scale_k_by_position,
+                                to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -242,3 +243,29 @@ def test_longest_first_and_grid_order_give_the_same_bits(pa, case):
         pa.pa_set_multi_order(1)
     assert np.all(np.isfinite(outs[0]))
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+RAMPS = [
+    # name, profile of the K row scale over positions: scores whose maxima climb steadily
+    # (many small moves of the softmax reference, and moves just under and past the lazy
+    # threshold), fall (the reference set early, later probabilities vanish), or jump
+    ("rising", lambda b, pos, L: 1.0 + pos / 40.0),
+    ("falling", lambda b, pos, L: 1.0 + (L - pos) / 40.0),
+    ("spikes", lambda b, pos, L: 60.0 if (pos * 7919 + b) % 389 == 0 else 1.0),
+]
+
+
+@pytest.mark.parametrize("ramp", RAMPS, ids=lambda r: r[0])
+@pytest.mark.parametrize("shape", ["chunks", "draft"])
+def test_score_ramps_through_the_softmax_reference(pa, oracle, shape, ramp):
+    """Score ranges of hundreds of log2 units: the chunk items' lazy reference and the stream
+    kernel's running maximum against the oracle."""
+    name, prof = ramp
+    if shape == "chunks":
+        wl = W.make_workload(f"ramp-{name}", 3, 32, 8, 128, 16, [1200, 2000, 700], W.BF16,
+                             seed=61, n_new=[600, 300, 700])
+    else:
+        wl = W.make_workload(f"ramp-{name}-draft", 6, 32, 8, 128, 16,
+                             [1200, 2000, 700, 64, 3000, 4], W.BF16, seed=62, n_new=[4] * 6)
+    scale_k_by_position(wl, prof)
+    _parity(pa, oracle, wl, f"{shape} {name}")
