@@ -217,7 +217,7 @@ def test_steps_built_by_the_product_allocator(pa, oracle):
     """Every table, slot and copy-on-write pair comes from the product allocator
     (pa_alloc_allocate / fork / append_token): four prompts (2040, 2048, 333 and 17 tokens,
     the first ending inside a block) are written by pa_reshape_and_cache, forked 16, 8, 4
-    and 2 ways, then every sequence appends three tokens, one per round, each round being
+    and 2 ways, then every sequence appends three tokens, one per step, each step being
     pa_copy_blocks (the clones its appends asked for) -> pa_reshape_and_cache; then
     pa_decode. Caches must equal the oracle's replay of the same calls bit for bit, and the
     output must match the oracle's attention."""
@@ -255,7 +255,7 @@ def test_steps_built_by_the_product_allocator(pa, oracle):
             slots.append(slot)
             if cow:
                 pairs.append(cow)
-        note(f"allocator-driven round {rnd}: {len(pairs)} clone pairs")
+        note(f"allocator-driven step {rnd}: {len(pairs)} clone pairs")
         if pairs:
             pairs = np.asarray(pairs, np.int32)
             st = pa.pa_validate_block_pairs(pairs, nb)
@@ -264,7 +264,7 @@ def test_steps_built_by_the_product_allocator(pa, oracle):
             kc, vc = oracle.copy_blocks(kc, vc, pairs)
             n_pairs += len(pairs)
         write(rand_rows(len(slots)), rand_rows(len(slots)), slots)
-    # round 0 clones the shared partial last blocks: 15 (2040 tokens), 3 (333) and 1 (17)
+    # step 0 clones the shared partial last blocks: 15 (2040 tokens), 3 (333) and 1 (17)
     assert n_pairs == 15 + 3 + 1
     B = len(tables)
     bt = np.zeros((B, max_blocks), np.int32)
