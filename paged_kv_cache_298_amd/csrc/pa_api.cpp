@@ -189,7 +189,7 @@ SharedWs shared_workspace(int32_t B, int32_t Hq, int32_t D, int32_t block_size, 
     SharedWs w;
     w.P = partition_tokens(block_size, max_blocks);
     const int64_t cap = (int64_t)block_size * max_blocks;
-    w.n_pre = (int32_t)((max_shared_tokens + pa_internal::kPrefixTokens - 1) / pa_internal::kPrefixTokens);
+    w.n_pre = (int32_t)(((int64_t)max_shared_tokens + pa_internal::kPrefixTokens - 1) / pa_internal::kPrefixTokens);
     w.n_suf = (int32_t)((cap + w.P - 1) / w.P);
     w.n_slots = w.n_pre + w.n_suf;
     const size_t rows = (size_t)B * (size_t)Hq * (size_t)w.n_slots;

@@ -236,6 +236,10 @@ def test_decode_shared_workspace_and_empty_batch():
     rows = 128 * 32 * n
     assert pa.pa_decode_shared_workspace_bytes(128, 32, 128, 16, 144, 2032) == _up(rows * 128 * 4) + rows * 8
     assert pa.pa_decode_shared_workspace_bytes(0, 32, 128, 16, 144, 2032) == 0
+    # the largest shared-token bound: its prefix-slot count is formed without overflow
+    big = (1 << 31) - 1
+    n = -(-big // 256) + -(-16 * 144 // P)
+    assert pa.pa_decode_shared_workspace_bytes(1, 8, 128, 16, 144, big) == _up(8 * n * 128 * 4) + 8 * n * 8
 
 
 def _multi(**kw):
