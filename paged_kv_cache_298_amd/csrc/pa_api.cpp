@@ -673,7 +673,7 @@ int32_t pa_reshape_and_cache(void* k_cache, void* v_cache, const void* key, cons
     if (T < 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0)
         return fail(PA_ERR_INVALID_ARG, "pa_reshape_and_cache: bad sizes T=%d Hkv=%d D=%d block_size=%d num_blocks=%d",
                     T, Hkv, D, block_size, num_blocks);
-    if ((D * eb) % 16 != 0 || D > 512)
+    if (D > 512 || (D * eb) % 16 != 0)
         return fail(PA_ERR_UNSUPPORTED, "pa_reshape_and_cache: head_dim %d (rows must be whole 16-byte units, <= 512)", D);
     if ((int64_t)num_blocks * block_size > 0x7fffffff)
         return fail(PA_ERR_UNSUPPORTED, "pa_reshape_and_cache: more than 2^31 slots");

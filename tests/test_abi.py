@@ -186,6 +186,8 @@ def test_cache_write_and_copy_validation():
     assert lib.pa_copy_blocks(None, None, None, 0, 8, 128, 16, 10, pa.PA_BF16, None) == 0
     assert lib.pa_reshape_and_cache(FAKE, FAKE, FAKE, FAKE, None, 4, 8, 128, 16, 10, pa.PA_BF16, None) == pa.PA_ERR_INVALID_ARG
     assert lib.pa_reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 12, 16, 10, pa.PA_BF16, None) == pa.PA_ERR_UNSUPPORTED
+    big_d = (1 << 31) - 1                      # rejected before its row size is formed
+    assert lib.pa_reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, big_d, 16, 10, pa.PA_F32, None) == pa.PA_ERR_UNSUPPORTED
     assert lib.pa_reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 9, None) == pa.PA_ERR_INVALID_ARG
     assert lib.pa_reshape_and_cache(FAKE, ctypes.c_void_p(0x100004), FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, pa.PA_BF16, None) == pa.PA_ERR_INVALID_ARG
     assert lib.pa_copy_blocks(FAKE, FAKE, None, 3, 8, 128, 16, 10, pa.PA_BF16, None) == pa.PA_ERR_INVALID_ARG
