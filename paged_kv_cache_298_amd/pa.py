@@ -118,6 +118,48 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(t, name, dtype, shape, device):
+    """t must be a tensor of this element type and shape (None: any extent) on `device`:
+    the library reads and writes by these sizes, so a mismatch would be read as other data
+    or written past the tensor."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != len(shape) or any(s is not None and s != d for s, d in zip(shape, t.shape)):
+        want = tuple("*" if s is None else s for s in shape)
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _expect_caches(k_cache, v_cache):
+    """The caches: [num_blocks, Hkv, block_size, D], same type and shape, on a GPU."""
+    if k_cache.dim() != 4:
+        raise ValueError(f"k_cache has shape {tuple(k_cache.shape)}, expected (num_blocks, Hkv, block_size, D)")
+    if not k_cache.is_cuda:
+        raise ValueError(f"the caches must be on a GPU, k_cache is on {k_cache.device}")
+    _kv_dtype(k_cache)
+    _expect(v_cache, "v_cache", k_cache.dtype, tuple(k_cache.shape), k_cache.device)
+    return k_cache.shape
+
+
+def _expect_decode(out, q, k_cache, v_cache, block_tables, seq_lens, workspace):
+    """Arguments of the decode entry points: out [B, Hq, D] fp32, q [B, Hq, D] and the caches
+    of one element type, block_tables int32 [B, max_blocks], seq_lens int32 [B]."""
+    nb, Hkv, bs, D = _expect_caches(k_cache, v_cache)
+    dev = k_cache.device
+    if q is None or q.dim() != 3:
+        raise ValueError("q must be [B, Hq, D]")
+    B, Hq = q.shape[0], q.shape[1]
+    _expect(q, "q", k_cache.dtype, (B, Hq, D), dev)
+    _expect(out, "out", torch.float32, (B, Hq, D), dev)
+    _expect(block_tables, "block_tables", torch.int32, (B, None), dev)
+    _expect(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    if workspace is not None:
+        _expect(workspace, "workspace", torch.uint8, (None,), dev)
+
+
 def _workspace(need, like, stream):
     """A workspace the library may fill as it likes (no zero fill, which would race with a
     launch on another stream), kept from reuse by torch's allocator until the work queued on
@@ -173,6 +215,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, workspace
     [num_blocks, Hkv, block_size, D]; block_tables int32 [B, max_blocks]; seq_lens int32 [B].
     workspace: a uint8 tensor of at least pa_decode_workspace_bytes(...) bytes (allocated
     here on q's device when None and needed)."""
+    _expect_decode(out, q, k_cache, v_cache, block_tables, seq_lens, workspace)
     B, Hq, D = q.shape
     nb, Hkv, bs, _ = k_cache.shape
     max_blocks = block_tables.shape[1]
@@ -192,7 +235,11 @@ def pa_decode_append(out, q, k_cache, v_cache, key, value, slot_mapping, block_t
     (slot_mapping int32 [B]: the slot of position seq_lens[b] - 1, or < 0 for none) and run
     pa_decode over the batch including it; the same result as pa_reshape_and_cache followed by
     pa_decode."""
+    _expect_decode(out, q, k_cache, v_cache, block_tables, seq_lens, workspace)
     B, Hq, D = q.shape
+    for name, t in (("key", key), ("value", value)):
+        _expect(t, name, k_cache.dtype, (B, k_cache.shape[1], D), k_cache.device)
+    _expect(slot_mapping, "slot_mapping", torch.int32, (B,), k_cache.device)
     nb, Hkv, bs, _ = k_cache.shape
     max_blocks = block_tables.shape[1]
     need = pa_decode_workspace_bytes(B, Hq, Hkv, D, bs, max_blocks, _kv_dtype(k_cache))
@@ -208,6 +255,7 @@ def pa_decode_append(out, q, k_cache, v_cache, key, value, slot_mapping, block_t
 
 def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, scale, stream=None):
     """pa_decode on the library's per-device scratch: no workspace, nothing allocated."""
+    _expect_decode(out, q, k_cache, v_cache, block_tables, seq_lens, None)
     B, Hq, D = q.shape
     nb, Hkv, bs, _ = k_cache.shape
     _check(_lib.pa_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
@@ -226,6 +274,9 @@ def pa_decode_shared(out, q, k_cache, v_cache, block_tables, seq_lens, groups, m
     """pa_decode for groups of consecutive sequences sharing their leading blocks.
     groups: int32 [n_groups, 3] on the device (first sequence, members, shared tokens),
     sorted by first sequence; max_members / max_shared_tokens: host bounds over the groups."""
+    _expect_decode(out, q, k_cache, v_cache, block_tables, seq_lens, workspace)
+    if groups is not None and groups.shape[0]:
+        _expect(groups, "groups", torch.int32, (None, 3), k_cache.device)
     B, Hq, D = q.shape
     nb, Hkv, bs, _ = k_cache.shape
     max_blocks = block_tables.shape[1]
@@ -253,6 +304,17 @@ def pa_decode_multi(out, q, k_cache, v_cache, block_tables, seq_lens, q_starts, 
     """Causal multi-query attention: q [total_q, Hq, D] holds each sequence's last n_b
     tokens (q_starts int32 [B + 1] on the device); query j of sequence b attends to tokens
     0 .. seq_lens[b] - n_b + j. max_q: host bound on any n_b."""
+    _, _, _, D = _expect_caches(k_cache, v_cache)
+    dev = k_cache.device
+    if q is None or q.dim() != 3:
+        raise ValueError("q must be [total_q, Hq, D]")
+    _expect(q, "q", k_cache.dtype, (q.shape[0], q.shape[1], D), dev)
+    _expect(out, "out", torch.float32, tuple(q.shape), dev)
+    _expect(seq_lens, "seq_lens", torch.int32, (None,), dev)
+    _expect(block_tables, "block_tables", torch.int32, (seq_lens.shape[0], None), dev)
+    _expect(q_starts, "q_starts", torch.int32, (seq_lens.shape[0] + 1,), dev)
+    if workspace is not None:
+        _expect(workspace, "workspace", torch.uint8, (None,), dev)
     total_q, Hq, D = q.shape
     nb, Hkv, bs, _ = k_cache.shape
     B = seq_lens.shape[0]
@@ -271,7 +333,10 @@ def pa_decode_multi(out, q, k_cache, v_cache, block_tables, seq_lens, q_starts, 
 
 def pa_reshape_and_cache(k_cache, v_cache, key, value, slot_mapping, stream=None):
     """Write key/value [T, Hkv, D] into the caches at slot_mapping int32 [T] (s < 0 skips)."""
-    nb, Hkv, bs, D = k_cache.shape
+    nb, Hkv, bs, D = _expect_caches(k_cache, v_cache)
+    _expect(slot_mapping, "slot_mapping", torch.int32, (None,), k_cache.device)
+    for name, t in (("key", key), ("value", value)):
+        _expect(t, name, k_cache.dtype, (slot_mapping.shape[0], Hkv, D), k_cache.device)
     T = slot_mapping.shape[0]
     _check(_lib.pa_reshape_and_cache(_ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value),
                                      _ptr(slot_mapping), T, Hkv, D, bs, nb, _kv_dtype(k_cache),
@@ -280,7 +345,8 @@ def pa_reshape_and_cache(k_cache, v_cache, key, value, slot_mapping, stream=None
 
 def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None):
     """Copy whole blocks src -> dst for each row of block_pairs int32 [N, 2]."""
-    nb, Hkv, bs, D = k_cache.shape
+    nb, Hkv, bs, D = _expect_caches(k_cache, v_cache)
+    _expect(block_pairs, "block_pairs", torch.int32, (None, 2), k_cache.device)
     N = block_pairs.shape[0]
     _check(_lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs), N, Hkv, D, bs, nb,
                                _kv_dtype(k_cache), _stream(k_cache, stream)))
@@ -295,8 +361,11 @@ def pa_read_tiles(k_cache, v_cache, tile_offsets, tile_bytes, sink, stream=None)
     sink (uint32 [READ_SINK_LEN]); no attention arithmetic."""
     if sink.dtype != torch.int32 or sink.numel() < READ_SINK_LEN:
         raise ValueError(f"sink must be an int32 tensor of at least {READ_SINK_LEN} entries")
-    if tile_offsets.dtype != torch.int64:
-        raise TypeError("tile_offsets must be int64")
+    if not k_cache.is_cuda:
+        raise ValueError(f"the caches must be on a GPU, k_cache is on {k_cache.device}")
+    _expect(v_cache, "v_cache", k_cache.dtype, tuple(k_cache.shape), k_cache.device)
+    _expect(tile_offsets, "tile_offsets", torch.int64, (None,), k_cache.device)
+    _expect(sink, "sink", torch.int32, (sink.numel(),), k_cache.device)
     _check(_lib.pa_read_tiles(_ptr(k_cache), _ptr(v_cache), k_cache.numel() * k_cache.element_size(),
                               _ptr(tile_offsets), tile_offsets.numel(), int(tile_bytes), _ptr(sink),
                               _stream(k_cache, stream)))

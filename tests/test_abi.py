@@ -204,6 +204,32 @@ def test_python_binding_marshals_dtypes():
         pa._ptr(torch.zeros(4, 4).t())
 
 
+def test_python_binding_checks_types_and_shapes():
+    """The wrappers refuse tensors whose type or shape differs from what the library reads
+    and writes (before any call into it)."""
+    import torch
+    i32 = torch.zeros(2, 3, dtype=torch.int32)
+    pa._expect(i32, "x", torch.int32, (2, None), None)
+    with pytest.raises(TypeError):
+        pa._expect(i32.long(), "x", torch.int32, (2, None), None)
+    with pytest.raises(ValueError):
+        pa._expect(i32, "x", torch.int32, (3, None), None)
+    with pytest.raises(ValueError):
+        pa._expect(i32, "x", torch.int32, (2, 3, 1), None)
+    with pytest.raises(ValueError):
+        pa._expect(None, "x", torch.int32, (2,), None)
+    # caches on the host are refused before the library is called
+    k = torch.zeros(4, 2, 16, 64, dtype=torch.bfloat16)
+    q = torch.zeros(3, 4, 64, dtype=torch.bfloat16)
+    out = torch.zeros(3, 4, 64)
+    bt = torch.zeros(3, 4, dtype=torch.int32)
+    sl = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        pa.pa_decode(out, q, k, k, bt, sl, 0.1)
+    with pytest.raises(ValueError, match="GPU"):
+        pa.pa_copy_blocks(k, k, torch.zeros(1, 2, dtype=torch.int32))
+
+
 def _shared(**kw):
     a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, groups=FAKE, ng=2, mm=4,
              msh=64, B=8, Hq=32, Hkv=8, D=128, bs=16, nb=64, mb=8, scale=0.1, dt=pa.PA_BF16,

@@ -650,3 +650,35 @@ def test_score_ramp_decode(pa, oracle, path):
     mode = pa.PA_PATH_STREAM if path == "stream" else pa.PA_PATH_PARTITION
     with _path(pa, mode, waves=64 if path == "stream" else 0):
         _parity(pa, oracle, wl, tag=f"ramp {path}")
+
+
+def test_binding_refuses_mismatched_tensors(pa):
+    """Tensors whose element type, shape or device differ from what the kernels read and
+    write are refused by the binding before any launch (a half-size fp16 output would
+    otherwise be written past its end; int64 tables would be read as other entries)."""
+    wl = W.make_workload("refuse", 3, 32, 8, 128, 16, [40, 300, 17], W.BF16, seed=3)
+    dw = DevWorkload(wl)
+    note("binding refuses mismatched tensors")
+    bad = [
+        dict(out=dw.out.half()),                              # output must be fp32
+        dict(out=dw.out[:2]),                                  # B rows
+        dict(q=dw.q.float()),                                  # q in the caches' type
+        dict(block_tables=dw.bt.long()),                       # int32 tables
+        dict(seq_lens=dw.sl[:2]),                              # one length per sequence
+        dict(seq_lens=dw.sl.cpu()),                            # on the caches' device
+        dict(v_cache=dw.v[:-1]),                               # same shape as k_cache
+    ]
+    base = dict(out=dw.out, q=dw.q, k_cache=dw.k, v_cache=dw.v, block_tables=dw.bt, seq_lens=dw.sl)
+    for change in bad:
+        args = dict(base, **change)
+        with pytest.raises((TypeError, ValueError)):
+            pa.pa_decode(args["out"], args["q"], args["k_cache"], args["v_cache"],
+                         args["block_tables"], args["seq_lens"], wl.scale)
+    with pytest.raises(ValueError):
+        pa.pa_reshape_and_cache(dw.k, dw.v, dw.nk[:2], dw.nv, dw.slots)
+    with pytest.raises(TypeError):
+        pa.pa_copy_blocks(dw.k, dw.v, torch.zeros((1, 2), dtype=torch.int64, device=DEV))
+    torch.cuda.synchronize()
+    # the correct call still runs
+    got = gpu_step(pa, dw)
+    assert np.isfinite(got).all()
