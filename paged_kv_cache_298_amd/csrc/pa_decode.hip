@@ -883,11 +883,15 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(Params p) {
     const int rec_a = 2 * (w - 1) + (d.z == s0p ? 0 : 1);
     // this wave's run of records [xa, xb) and its float4s of the row, i0 + lane + 64 f
     int xa = 0, xb = nrec, i0 = 0;
+    // a run that fits one batch is merged by wave 0 alone, with no exchange through LDS
+    // (uniform over the workgroup: every wave reads the same descriptor)
+    const bool single = !COLSPLIT && nrec <= kBatch;
     if constexpr (COLSPLIT) {
         i0 = wid * 64 * F;
     } else {
-        const int per = (nrec + 3) >> 2;
-        xa = min(nrec, wid * per);
+        if (single && wid != 0) return;
+        const int per = single ? nrec : (nrec + 3) >> 2;
+        xa = single ? 0 : min(nrec, wid * per);
         xb = min(nrec, xa + per);
     }
     int hh[F], cc[F];                  // head and float4 column of each of the lane's float4s
@@ -971,9 +975,10 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(Params p) {
         reinterpret_cast<float4*>(p.out + orow * D)[c4] =
             make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     };
-    if constexpr (COLSPLIT) {
+    if (COLSPLIT || single) {
 #pragma unroll
-        for (int f = 0; f < F; ++f) store(i0 + lane + 64 * f, o[f], l[f]);
+        for (int f = 0; f < F; ++f)
+            if (i0 + lane + 64 * f < NF) store(i0 + lane + 64 * f, o[f], l[f]);
     } else {
         __shared__ float4 s_o[4][NF];
         __shared__ float2 s_ml[4][NF];
