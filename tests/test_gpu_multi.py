@@ -269,3 +269,29 @@ def test_score_ramps_through_the_softmax_reference(pa, oracle, shape, ramp):
                              [1200, 2000, 700, 64, 3000, 4], W.BF16, seed=62, n_new=[4] * 6)
     scale_k_by_position(wl, prof)
     _parity(pa, oracle, wl, f"{shape} {name}")
+
+
+LONG = [
+    # name, lens, n_new: a 16,384-token prompt as one prefill (1,024 query tiles per KV
+    # head, one partition), a 2,048-token chunk at the end of a 32,768-token context, and a
+    # 256-token chunk there (few tiles: the context is cut into partitions, then merged)
+    ("prefill-16k", [16384], [16384]),
+    ("chunk-at-32k", [32768, 900], [2048, 100]),
+    ("short-chunk-at-32k", [32768, 900], [256, 100]),
+]
+
+
+@pytest.mark.parametrize("case", LONG, ids=lambda c: c[0])
+def test_long_prefill_and_late_chunk(pa, oracle, case):
+    """The longest query ranges: every (query, head) row is computed on the GPU and 512
+    rows spread over the whole range (the first and last of each sequence included) are
+    compared with the oracle one by one."""
+    name, lens, n_new = case
+    wl = W.make_workload(f"mq-{name}", len(lens), 32, 8, 128, 16, lens, W.BF16,
+                         seed=sum(lens), n_new=n_new)
+    total = int(wl.q_starts[-1])
+    rng = np.random.default_rng(7)
+    firsts = [int(wl.q_starts[b]) * wl.Hq for b in range(wl.B)]
+    lasts = [int(wl.q_starts[b + 1]) * wl.Hq - 1 for b in range(wl.B)]
+    rows = np.unique(np.concatenate([firsts, lasts, rng.integers(0, total * wl.Hq, size=508)]))
+    _parity(pa, oracle, wl, name, rows=rows.astype(np.int32))
